@@ -1,0 +1,301 @@
+"""SGMV benchmark on one MI355X: shrink + expand (or fused) per call, through
+the C ABI, on seeded synthetic batches resident in HBM.
+
+Default workload: decode with distinct adapters (d_in = d_out = 4096,
+r = 16, alpha = 32, 64 tokens in 64 length-1 segments, adapters drawn without
+replacement from a pool of 256, bf16). One step is one call of the hot path
+over one batch. To keep the 256 MB Infinity Cache from serving the weights,
+the steps rotate over R replicas of the pools and activations (each its own
+HBM region), so a replica's bytes are cold when it comes round again.
+
+Prints ONE JSON line: value = algorithmic HBM GB/s (X read once, each
+segment's adapter read once, Y read and written once) over the timed steps,
+plus a roofline object for the dominant kernel and the CPU oracle's rate on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGMV shrink+expand µs/call and HBM GB/s (% peak), 4096-d r=16, 64 adapters"
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default="decode_distinct",
+                   choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b"])
+    p.add_argument("--path", default="split", choices=["split", "fused"])
+    p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run one plain device copy of this size (for counter scaling)")
+    return p.parse_args()
+
+
+class Replica:
+    """One HBM-resident copy of a workload's inputs (device tensors)."""
+
+    def __init__(self, w, dev, A_pool, B_pool, X, Y):
+        import torch
+        import segmented_gather_gemm_sgmv_amd as sg
+        self.w = w
+        self.X, self.Y = X, Y
+        # the pools must outlive the device tables that point into them
+        self.A_pool, self.B_pool = A_pool, B_pool
+        self.A_ptrs = sg.sgmv_pool_pointers(A_pool)
+        self.B_ptrs = sg.sgmv_pool_pointers(B_pool)
+        self.seg_start = torch.from_numpy(np.ascontiguousarray(w.seg_start, np.int32)).to(dev)
+        self.seg_adapter = torch.from_numpy(np.ascontiguousarray(w.seg_adapter, np.int32)).to(dev)
+        self.V = torch.zeros((w.M, w.r), dtype=torch.float32, device=dev)
+
+
+def make_workloads(name):
+    from tests import workloads as wl
+    import segmented_gather_gemm_sgmv_amd as sg
+    if name == "tiny":
+        return [wl.tiny()]
+    if name == "decode_distinct":
+        return [wl.decode_distinct(pool=False)]
+    if name == "decode_skewed":
+        return [wl.decode_skewed(sg.sgmv_build_segments)]
+    if name == "prefill":
+        return [wl.prefill()]
+    return wl.slice70b()
+
+
+def build_replicas(ws, dev, R):
+    """R replicas of every projection's inputs. Pools are drawn on the device
+    (seeded); X is the workload's own seeded draw."""
+    import torch
+    from tests import workloads as wl
+    reps = []
+    for q in range(R):
+        group = []
+        for w in ws:
+            A = wl.device_pool(w.num_adapters, w.r, w.d_in, w.d_in ** -0.5, w.seed * 7 + 2 * q + 1, dev)
+            B = wl.device_pool(w.num_adapters, w.r, w.d_out, w.r ** -0.5, w.seed * 7 + 2 * q + 2, dev)
+            if w.dtype == torch.float32:
+                A, B = A.float(), B.float()
+            X = w.X.to(dev)
+            Y = w.Y.to(dev)
+            group.append(Replica(w, dev, A, B, X, Y))
+        reps.append(group)
+    return reps
+
+
+def step(group, path, ws=None):
+    import segmented_gather_gemm_sgmv_amd as sg
+    for rp in group:
+        w = rp.w
+        if path == "fused":
+            sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
+                          workspace_buf=ws)
+        else:
+            sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r)
+            sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
+
+
+def capture(reps, path, first, count, ws):
+    """A HIP graph of `count` consecutive steps starting at replica `first`:
+    replaying it launches the kernels back to back with no host work."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            step(reps[(first + i) % len(reps)], path, ws)
+    return g
+
+
+def kernel_bytes(w, path):
+    """Algorithmic bytes per launch of each kernel of the path."""
+    e = 4 if str(w.dtype).endswith("float32") else 2
+    N = w.num_segments
+    x = e * w.M * w.d_in
+    a = e * N * w.r * w.d_in
+    b = e * N * w.r * w.d_out
+    y = 2 * e * w.M * w.d_out
+    v = 4 * w.M * w.r
+    if path == "fused":
+        return {"fused": x + a + b + y}
+    return {"shrink": x + a + v, "expand": b + y + v}
+
+
+def time_kernels(reps, path, steps, wsbuf):
+    """Average duration of each kernel of the path, from HIP events recorded
+    around every launch on the stream the kernels run on."""
+    import torch
+    import segmented_gather_gemm_sgmv_amd as sg
+    stream = torch.cuda.current_stream()
+    names = ["fused"] if path == "fused" else ["shrink", "expand"]
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        group = reps[i % len(reps)]
+        for rp in group:
+            w = rp.w
+            if path == "fused":
+                evs[i][0][0].record(stream)
+                sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
+                              workspace_buf=wsbuf)
+                evs[i][0][1].record(stream)
+            else:
+                evs[i][0][0].record(stream)
+                sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r)
+                evs[i][0][1].record(stream)
+                evs[i][1][0].record(stream)
+                sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
+                evs[i][1][1].record(stream)
+    torch.cuda.synchronize()
+    out = {}
+    for j, n in enumerate(names):
+        out[n] = float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
+    return out  # microseconds
+
+
+def cpu_baseline(ws, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole batches of the first projection, repeated for about `seconds`."""
+    import torch
+    import oracle
+    from tests import workloads as wl
+    orc = oracle.get()
+    w = ws[0]
+    rng = np.random.Generator(np.random.PCG64(99))
+    if w.A_pool is None:
+        # only the touched slots matter to the oracle: draw those, remap ids
+        N = w.num_segments
+        A = wl._normal(rng, (N, w.r, w.d_in), w.d_in ** -0.5, w.dtype)
+        B = wl._normal(rng, (N, w.r, w.d_out), w.r ** -0.5, w.dtype)
+        seg_adapter = np.arange(N, dtype=np.int32)
+    else:
+        A, B, seg_adapter = w.A_pool, w.B_pool, w.seg_adapter
+    args = (wl.storage(w.Y), wl.storage(w.X), wl.storage(A), wl.storage(B), w.seg_start, seg_adapter, w.alpha)
+    orc.sgmv(*args)  # warm
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.sgmv(*args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_call = el / reps
+    nbytes = w.algorithmic_bytes()
+    return {"value": nbytes / per_call / 1e9, "unit": "GB/s", "cores": oracle.threads_used(),
+            "kind": "oracle", "us_per_call": per_call * 1e6,
+            "sample": f"{reps} whole {w.name} batches ({w.M} rows, {w.num_segments} segments), "
+                      f"{el:.1f} s of CPU work"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU split is described, not built)"}))
+        sys.exit(2)
+    import torch
+    import segmented_gather_gemm_sgmv_amd as sg
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    ws = make_workloads(args.workload)
+    touched = sum(w.algorithmic_bytes() for w in ws)
+    R = args.replicas or max(1, min(256, -(-(1 << 30) // touched)))
+    reps = build_replicas(ws, dev, R)
+    torch.cuda.synchronize()
+
+    # one zero-filled workspace serves every fused call (they run in order on
+    # one stream and each returns the control words to zero)
+    need = max(sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype) for w in ws)
+    wsbuf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    for i in range(args.warmup):
+        step(reps[i % R], args.path, wsbuf)
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps, replayed from HIP graphs (one graph
+    # over all R replicas, plus one for the remainder).
+    full = capture(reps, args.path, 0, R, wsbuf) if args.steps >= R else None
+    rem = args.steps % R if args.steps >= R else args.steps
+    tail = capture(reps, args.path, 0, rem, wsbuf) if rem else None
+    if full is not None:
+        full.replay()  # untimed replay: page in the graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps // R if full is not None else 0):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # per-kernel durations (events around each launch), for the roofline
+    kus = time_kernels(reps, args.path, min(args.steps, 1000), wsbuf)
+    per_kernel = kernel_bytes(ws[0], args.path)
+    if len(ws) > 1:  # several projections: sum their bytes per kernel name
+        for w in ws[1:]:
+            for n, b in kernel_bytes(w, args.path).items():
+                per_kernel[n] += b
+    dom = max(kus, key=kus.get)   # the kernel that takes the most time per step
+    achieved = per_kernel[dom] / (kus[dom] * 1e-6) / 1e9
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = sum(w.algorithmic_bytes() for w in ws)
+    flops = sum(w.flops() for w in ws)
+    w0 = ws[0]
+    value = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_call": ms * 1e3,
+        "tokens_per_s": w0.M / (ms * 1e-3),
+        "hbm_frac": value / HBM_PEAK_GBS,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w0.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "path": "shrink+expand" if args.path == "split" else "fused",
+                   "d_in": w0.d_in, "d_out": w0.d_out, "r": w0.r, "alpha": w0.alpha, "tokens": w0.M,
+                   "segments": w0.num_segments, "pool": w0.num_adapters, "projections": len(ws),
+                   "replicas": R, "algorithmic_bytes_per_step": nbytes},
+        "kernels_us": kus,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * sgmv.h — C ABI of the MI355X (gfx950) SGMV library.
+ *
+ * SGMV (segmented gather matrix-vector multiplication) applies many LoRA
+ * adapters to one batch in one pass. The batch's rows are grouped into
+ * contiguous segments; segment s covers rows seg_start[s] .. seg_start[s+1]-1
+ * and uses adapter k = seg_adapter[s] from a pool reached through a table of
+ * pointers. For every row m of segment s:
+ *
+ *     V[m, :] = X[m, :] . A_k                         (shrink, d_in -> r)
+ *     Y[m, :] = Y[m, :] + (alpha / r) * V[m, :] . B_k  (expand, r -> d_out)
+ *
+ * Sources (Punica guide, aifetchly blog): the per-row LoRA equation for y_i
+ * in section "The Heterogeneous Batching Bottleneck" (delta added to the base
+ * output, scaled by alpha / r, A_k of logical shape d_in x r, B_k of logical
+ * shape r x d_out); the segment offsets S = {s_0 .. s_N} and the pointer
+ * array of section "The SGMV Mathematical Formulation"; the single kernel
+ * that takes X and the pointers to A and B (figure "Punica: SGMV"); the two
+ * launches per layer, one for all A and one for all B (section "Mathematical
+ * Modeling", equation 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * dtype        SGMV_F32 or SGMV_BF16. X, Y and every adapter share it. V is
+ *              always fp32. Arithmetic accumulates in fp32; Y is rounded once,
+ *              to nearest-even, when stored.
+ * X            device, row-major M x d_in, contiguous, 16-byte aligned.
+ * Y            device, row-major M x d_out, contiguous, 16-byte aligned;
+ *              read and written (the delta is added to what Y holds).
+ * V            device, row-major M x r fp32, contiguous, 16-byte aligned.
+ * A_ptrs       device array of num_adapters 64-bit device addresses. Entry k
+ *              points to A_k stored as r rows of d_in elements: logical
+ *              element (i, j) of A_k sits at j * d_in + i. 16-byte aligned.
+ * B_ptrs       device array of num_adapters addresses. Entry k points to B_k
+ *              stored as r rows of d_out elements: (j, n) at j * d_out + n.
+ * seg_start    device int32[num_segments + 1], non-decreasing, with
+ *              seg_start[0] = 0 and seg_start[num_segments] = M.
+ * seg_adapter  device int32[num_segments], each in [0, num_adapters).
+ * r            8, 16, 32 or 64.
+ * d_in, d_out  positive multiples of 8.
+ * stream       a hipStream_t (NULL = the default stream). Every call is
+ *              asynchronous and stream-ordered: it only enqueues kernels, makes
+ *              no host<->device copy and no synchronisation.
+ *
+ * Ownership: the caller owns every buffer and must keep it alive until the
+ * stream work completes. The library allocates no memory and keeps no pointer
+ * after a call returns.
+ *
+ * Errors: every call returns SGMV_OK (0) or a negative status; no call
+ * aborts. Arguments are checked on the host before anything is enqueued; on
+ * error nothing is enqueued. M == 0 or num_segments == 0 is a successful
+ * no-op. Device-resident metadata cannot be checked without a
+ * synchronisation, so the kernels defend themselves instead: segment bounds
+ * are clamped into [0, M] (a non-increasing pair is an empty segment) and a
+ * segment whose adapter id lies outside [0, num_adapters) is skipped (its rows
+ * are left as they were). Nothing outside the documented buffers is read or
+ * written for any metadata values.
+ */
+#ifndef SGMV_H
+#define SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sgmv_dtype { SGMV_F32 = 0, SGMV_BF16 = 1 };
+
+enum sgmv_status {
+    SGMV_OK = 0,
+    SGMV_ERR_NULL = -1,      /* a required pointer is NULL */
+    SGMV_ERR_SHAPE = -2,     /* negative size, d not a multiple of 8, or too large */
+    SGMV_ERR_RANK = -3,      /* r not in {8, 16, 32, 64} */
+    SGMV_ERR_DTYPE = -4,     /* dtype not SGMV_F32 / SGMV_BF16 */
+    SGMV_ERR_ALIGN = -5,     /* X, Y or V not 16-byte aligned */
+    SGMV_ERR_WORKSPACE = -6, /* workspace missing or smaller than sgmv_workspace_bytes */
+    SGMV_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
+    SGMV_ERR_ADAPTER = -8    /* host metadata: a negative adapter id */
+};
+
+/*
+ * Shrink (Punica guide, "The SGMV Mathematical Formulation": one launch for
+ * every segment; "Mathematical Modeling" eq. 2: the launch for all A).
+ * V[m, j] = sum_i X[m, i] * A_k(i, j) for every row m of every segment.
+ * V is overwritten for rows that lie in a segment with a valid adapter, and
+ * left untouched elsewhere.
+ */
+int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *stream);
+
+/*
+ * Expand (same sources; the launch for all B, and the equation for y_i: the
+ * delta, scaled by alpha / r, is added to the base output).
+ * Y[m, n] += (alpha / r) * sum_j V[m, j] * B_k(j, n). The scale alpha / r is
+ * formed once in fp32.
+ */
+int sgmv_expand(void *Y, const float *V, const uint64_t *B_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_out, int32_t r, float alpha, int32_t dtype, void *stream);
+
+/*
+ * Fused shrink + expand in one launch (Punica guide, figure "Punica: SGMV":
+ * one kernel call over X and the pointers to A and B).
+ * Y[m, :] += (alpha / r) * X[m, :] . A_k . B_k. The intermediate V lives in
+ * the workspace and is not returned. Same result as sgmv_shrink followed by
+ * sgmv_expand, up to fp32 summation order.
+ *
+ * workspace: device memory of at least sgmv_workspace_bytes(...) bytes,
+ * 256-byte aligned, zero-filled before its first use (for example by
+ * hipMemset once after allocating it). Every call returns it to all-zero
+ * control words when its kernel completes, so it can be reused by later calls
+ * on the same stream without clearing. Calls that overlap in time (different
+ * streams) must use different workspaces.
+ */
+int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+               int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+               int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
+               float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* Bytes of workspace sgmv_fused needs for these sizes (0 on invalid sizes). */
+size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
+                            int32_t r, int32_t dtype);
+
+/*
+ * Host-side segment metadata (Punica guide, "Hardware-Level Optimizations in
+ * SGMV": requests are grouped by adapter so that each adapter's rows are
+ * contiguous; "The SGMV Mathematical Formulation": the offsets s_0 .. s_N).
+ *
+ * token_adapter: host int32[M], the adapter of each token, each >= 0.
+ * perm:          host int32[M], out: the stable sort of token indices by
+ *                adapter id; row p of the segmented batch is token perm[p].
+ * seg_start:     host int32[M + 1], out: the first *num_segments + 1 entries
+ *                are the segment offsets (seg_start[0] = 0, last = M).
+ * seg_adapter:   host int32[M], out: the first *num_segments entries are the
+ *                segments' adapter ids, strictly increasing.
+ * num_segments:  host int32, out: the number of distinct adapters.
+ * Returns SGMV_ERR_ADAPTER if an id is negative, SGMV_ERR_NULL / _SHAPE on
+ * bad arguments. Runs in O(M log M) on the calling thread.
+ */
+int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
+                        int32_t *seg_start, int32_t *seg_adapter, int32_t *num_segments);
+
+/*
+ * Adapter pool pointer table (Punica guide, figure "SGMV Kernel Memory
+ * Layout": an array of pointers, each to one adapter's contiguous memory;
+ * section "Core Innovation 2": one unified device buffer holds the hot
+ * adapters). Fills ptrs_host[k] = base + k * slot_bytes for k < num_adapters,
+ * for a pool whose slots are packed back to back. The caller copies the table
+ * to the device. Tables for scattered slots may be filled by the caller
+ * directly with any 16-byte aligned device addresses.
+ */
+int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,
+                       int64_t slot_bytes);
+
+/* A static, human-readable name for a status code. */
+const char *sgmv_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sgmv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGMV_H */

@@ -1,0 +1,211 @@
+"""Python binding of libsgmv.so, the MI355X SGMV library (C ABI in
+``include/sgmv.h``).
+
+Argument marshalling only: every function below checks tensor placement,
+dtype and contiguity, passes raw device pointers, sizes and the current HIP
+stream to the C function of the same name, and raises on a non-zero status.
+All arithmetic runs in the library's gfx950 kernels. PyTorch supplies device
+memory and streams.
+
+If ``libsgmv.so`` has not been built, importing this package raises
+``ImportError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+_HERE = Path(__file__).resolve().parent
+LIBRARY = _HERE / "libsgmv.so"
+
+SGMV_F32 = 0
+SGMV_BF16 = 1
+SGMV_OK = 0
+
+_DTYPES = {torch.float32: SGMV_F32, torch.bfloat16: SGMV_BF16}
+
+# (name, restype, argtypes) for every symbol include/sgmv.h declares.
+_i32, _i64, _vp, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+EXPORTS = {
+    "sgmv_shrink": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "sgmv_expand": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "sgmv_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _f32, _i32, _vp, _sz, _vp]),
+    "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
+    "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
+    "sgmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sgmv_version": (ctypes.c_int, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not LIBRARY.exists():
+        raise ImportError(f"{LIBRARY} is not built; run `python -m segmented_gather_gemm_sgmv_amd.build`")
+    lib = ctypes.CDLL(str(LIBRARY))
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class SGMVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {lib.sgmv_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SGMV_OK:
+        raise SGMVError(fn, status)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, dim=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def sgmv_shrink(V: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, seg_start: torch.Tensor,
+                seg_adapter: torch.Tensor, r: int, stream=None) -> torch.Tensor:
+    """V[M, r] (fp32, overwritten per segment row) = X[M, d_in] . A_k."""
+    M, d_in = X.shape
+    if V.shape != (M, r):
+        raise ValueError("V must be M x r")
+    st = lib.sgmv_shrink(_dev(V, "V", torch.float32, 2), _dev(X, "X", dim=2),
+                         _dev(A_ptrs, "A_ptrs", torch.int64, 1), A_ptrs.numel(),
+                         _dev(seg_start, "seg_start", torch.int32, 1),
+                         _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                         M, d_in, r, _dtype_code(X), _stream(X, stream))
+    _check("sgmv_shrink", st)
+    return V
+
+
+def sgmv_expand(Y: torch.Tensor, V: torch.Tensor, B_ptrs: torch.Tensor, seg_start: torch.Tensor,
+                seg_adapter: torch.Tensor, r: int, alpha: float, stream=None) -> torch.Tensor:
+    """Y[M, d_out] += (alpha / r) * V . B_k per segment (in place)."""
+    M, d_out = Y.shape
+    if V.shape != (M, r):
+        raise ValueError("V must be M x r")
+    st = lib.sgmv_expand(_dev(Y, "Y", dim=2), _dev(V, "V", torch.float32, 2),
+                         _dev(B_ptrs, "B_ptrs", torch.int64, 1), B_ptrs.numel(),
+                         _dev(seg_start, "seg_start", torch.int32, 1),
+                         _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                         M, d_out, r, float(alpha), _dtype_code(Y), _stream(Y, stream))
+    _check("sgmv_expand", st)
+    return Y
+
+
+def sgmv_workspace_bytes(num_segments: int, M: int, d_in: int, d_out: int, r: int,
+                         dtype: torch.dtype) -> int:
+    return int(lib.sgmv_workspace_bytes(num_segments, M, d_in, d_out, r, _DTYPES[dtype]))
+
+
+_workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def workspace(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
+    """A zero-filled workspace for sgmv_fused, cached per (device, stream).
+
+    The fused kernel returns its control words to zero when it completes, so
+    one buffer serves every later call on the same stream."""
+    device = torch.device(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           _stream(torch.empty(0, device=device), stream))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def sgmv_fused(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: torch.Tensor,
+               seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int, alpha: float,
+               workspace_buf: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y += (alpha / r) * X . A_k . B_k per segment, in one launch (in place)."""
+    M, d_in = X.shape
+    M2, d_out = Y.shape
+    if M2 != M:
+        raise ValueError("X and Y must have the same number of rows")
+    if A_ptrs.numel() != B_ptrs.numel():
+        raise ValueError("A_ptrs and B_ptrs must have one entry per adapter")
+    need = sgmv_workspace_bytes(seg_adapter.numel(), M, d_in, d_out, r, X.dtype)
+    if workspace_buf is None:
+        workspace_buf = workspace(X.device, need, stream)
+    st = lib.sgmv_fused(_dev(Y, "Y", dim=2), _dev(X, "X", dim=2),
+                        _dev(A_ptrs, "A_ptrs", torch.int64, 1), _dev(B_ptrs, "B_ptrs", torch.int64, 1),
+                        A_ptrs.numel(), _dev(seg_start, "seg_start", torch.int32, 1),
+                        _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                        M, d_in, d_out, r, float(alpha), _dtype_code(X),
+                        _dev(workspace_buf, "workspace"), workspace_buf.numel() * workspace_buf.element_size(),
+                        _stream(X, stream))
+    _check("sgmv_fused", st)
+    return Y
+
+
+def sgmv_build_segments(token_adapter) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Host: group tokens by adapter. Returns (perm, seg_start, seg_adapter)."""
+    ids = np.ascontiguousarray(np.asarray(token_adapter, dtype=np.int32))
+    M = int(ids.shape[0])
+    perm = np.empty(M, np.int32)
+    seg_start = np.empty(M + 1, np.int32)
+    seg_adapter = np.empty(max(M, 1), np.int32)
+    n = ctypes.c_int32(0)
+    st = lib.sgmv_build_segments(ids.ctypes.data, M, perm.ctypes.data, seg_start.ctypes.data,
+                                 seg_adapter.ctypes.data, ctypes.byref(n))
+    _check("sgmv_build_segments", st)
+    return perm, seg_start[: n.value + 1].copy(), seg_adapter[: n.value].copy()
+
+
+def sgmv_pool_pointers(pool: torch.Tensor) -> torch.Tensor:
+    """Device table (int64) of slot addresses of a packed pool tensor P x r x d.
+
+    The table holds a reference to ``pool``, so the memory it points into
+    cannot be freed while the table is alive."""
+    if pool.dim() != 3 or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous P x r x d tensor")
+    P = pool.shape[0]
+    table = np.empty(max(P, 1), np.uint64)
+    slot_bytes = pool.shape[1] * pool.shape[2] * pool.element_size()
+    st = lib.sgmv_pool_pointers(table.ctypes.data, ctypes.c_void_p(pool.data_ptr()), P, slot_bytes)
+    _check("sgmv_pool_pointers", st)
+    out = torch.from_numpy(table[:P].view(np.int64).copy()).to(pool.device)
+    out._sgmv_pool = pool
+    return out
+
+
+def sgmv_version() -> int:
+    return int(lib.sgmv_version())
+
+
+__all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_workspace_bytes", "sgmv_build_segments",
+           "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
+           "LIBRARY", "SGMV_F32", "SGMV_BF16"]

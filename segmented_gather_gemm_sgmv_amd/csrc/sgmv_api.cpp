@@ -1,0 +1,148 @@
+// The C ABI declared in include/sgmv.h: argument checks, dispatch to the
+// gfx950 kernels, and the host-side metadata helpers.
+#include "sgmv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "sgmv_launch.h"
+
+namespace {
+
+bool valid_rank(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+bool valid_dtype(int32_t dt) { return dt == SGMV_F32 || dt == SGMV_BF16; }
+bool valid_dim(int32_t d) { return d > 0 && d % 8 == 0; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element count one operand may span: indices are formed in 64-bit
+// arithmetic, but a segment's row count and a column index stay in int.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+int check_common(int32_t num_adapters, int32_t num_segments, int32_t M, int32_t r,
+                 int32_t dtype) {
+    if (!valid_dtype(dtype)) return SGMV_ERR_DTYPE;
+    if (!valid_rank(r)) return SGMV_ERR_RANK;
+    if (M < 0 || num_segments < 0 || num_adapters < 0) return SGMV_ERR_SHAPE;
+    return SGMV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sgmv_version(void) { return 100; }
+
+const char *sgmv_status_string(int status) {
+    switch (status) {
+        case SGMV_OK: return "ok";
+        case SGMV_ERR_NULL: return "a required pointer is NULL";
+        case SGMV_ERR_SHAPE: return "invalid size (negative, not a multiple of 8, or too large)";
+        case SGMV_ERR_RANK: return "rank must be 8, 16, 32 or 64";
+        case SGMV_ERR_DTYPE: return "dtype must be SGMV_F32 or SGMV_BF16";
+        case SGMV_ERR_ALIGN: return "X, Y and V must be 16-byte aligned";
+        case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
+        case SGMV_ERR_HIP: return "HIP runtime error at launch";
+        case SGMV_ERR_ADAPTER: return "negative adapter id";
+        default: return "unknown status";
+    }
+}
+
+size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
+                            int32_t r, int32_t dtype) {
+    if (num_segments < 0 || M < 0 || !valid_dim(d_in) || !valid_dim(d_out) || !valid_rank(r) ||
+        !valid_dtype(dtype))
+        return 0;
+    return sgmv::fused_layout(num_segments, M, r).total;
+}
+
+int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *stream) {
+    int st = check_common(num_adapters, num_segments, M, r, dtype);
+    if (st != SGMV_OK) return st;
+    if (!valid_dim(d_in) || (int64_t)M * d_in > kMaxElems) return SGMV_ERR_SHAPE;
+    if (M == 0 || num_segments == 0) return SGMV_OK;
+    if (!V || !X || !A_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!aligned16(V) || !aligned16(X)) return SGMV_ERR_ALIGN;
+    sgmv::ShrinkArgs a{V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
+                       num_segments, M, d_in, r, dtype};
+    return hip_status(sgmv::launch_shrink(a, static_cast<hipStream_t>(stream)));
+}
+
+int sgmv_expand(void *Y, const float *V, const uint64_t *B_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_out, int32_t r, float alpha, int32_t dtype, void *stream) {
+    int st = check_common(num_adapters, num_segments, M, r, dtype);
+    if (st != SGMV_OK) return st;
+    if (!valid_dim(d_out) || (int64_t)M * d_out > kMaxElems) return SGMV_ERR_SHAPE;
+    if (M == 0 || num_segments == 0) return SGMV_OK;
+    if (!Y || !V || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!aligned16(Y) || !aligned16(V)) return SGMV_ERR_ALIGN;
+    sgmv::ExpandArgs a{Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments,
+                       M, d_out, r, dtype, alpha / (float)r};
+    return hip_status(sgmv::launch_expand(a, static_cast<hipStream_t>(stream)));
+}
+
+int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+               int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+               int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
+               float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+               void *stream) {
+    int st = check_common(num_adapters, num_segments, M, r, dtype);
+    if (st != SGMV_OK) return st;
+    if (!valid_dim(d_in) || !valid_dim(d_out) || (int64_t)M * d_in > kMaxElems ||
+        (int64_t)M * d_out > kMaxElems)
+        return SGMV_ERR_SHAPE;
+    if (M == 0 || num_segments == 0) return SGMV_OK;
+    if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < sgmv_workspace_bytes(num_segments, M, d_in, d_out, r, dtype))
+        return SGMV_ERR_WORKSPACE;
+    sgmv::FusedArgs a{Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
+                      num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, workspace};
+    return hip_status(sgmv::launch_fused(a, static_cast<hipStream_t>(stream)));
+}
+
+int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
+                        int32_t *seg_start, int32_t *seg_adapter, int32_t *num_segments) {
+    if (M < 0) return SGMV_ERR_SHAPE;
+    if (!num_segments || !seg_start || (M > 0 && (!token_adapter || !perm || !seg_adapter)))
+        return SGMV_ERR_NULL;
+    for (int32_t i = 0; i < M; ++i)
+        if (token_adapter[i] < 0) return SGMV_ERR_ADAPTER;
+    std::iota(perm, perm + M, 0);
+    std::stable_sort(perm, perm + M, [token_adapter](int32_t a, int32_t b) {
+        return token_adapter[a] < token_adapter[b];
+    });
+    int32_t n = 0;
+    for (int32_t p = 0; p < M; ++p) {
+        const int32_t id = token_adapter[perm[p]];
+        if (p == 0 || id != token_adapter[perm[p - 1]]) {
+            seg_start[n] = p;
+            seg_adapter[n] = id;
+            ++n;
+        }
+    }
+    seg_start[n] = M;
+    *num_segments = n;
+    return SGMV_OK;
+}
+
+int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,
+                       int64_t slot_bytes) {
+    if (num_adapters < 0 || slot_bytes < 0) return SGMV_ERR_SHAPE;
+    if (num_adapters == 0) return SGMV_OK;
+    if (!ptrs_host || !base) return SGMV_ERR_NULL;
+    if ((slot_bytes & 15) != 0 || !aligned16(base)) return SGMV_ERR_ALIGN;
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    for (int32_t k = 0; k < num_adapters; ++k) ptrs_host[k] = b + (uint64_t)k * (uint64_t)slot_bytes;
+    return SGMV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Shared device helpers for the SGMV kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgmv {
+
+constexpr int kWave = 64;
+
+// Storage element types. bf16 is kept as raw 16-bit patterns and widened by a
+// shift; fp32 is used as is.
+struct bf16_t {
+    uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;  // elements per 16-byte vector
+};
+template <>
+struct Elem<bf16_t> {
+    static constexpr int kPerVec = 8;
+};
+
+// 16-byte vector load/store through the vector memory path.
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming load: weights are read once per call, so keep them out of the way
+// of data that is reused.
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Widen one 16-byte vector to fp32 values.
+template <typename T>
+__device__ __forceinline__ void widen(uint4 v, float (&out)[Elem<T>::kPerVec]);
+
+template <>
+__device__ __forceinline__ void widen<float>(uint4 v, float (&out)[4]) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+}
+
+template <>
+__device__ __forceinline__ void widen<bf16_t>(uint4 v, float (&out)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Narrow fp32 values to one 16-byte vector, rounding to nearest-even.
+template <typename T>
+__device__ __forceinline__ uint4 narrow(const float (&in)[Elem<T>::kPerVec]);
+
+template <>
+__device__ __forceinline__ uint4 narrow<float>(const float (&in)[4]) {
+    return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                      __float_as_uint(in[3]));
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t p = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32: round to nearest-even
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+template <>
+__device__ __forceinline__ uint4 narrow<bf16_t>(const float (&in)[8]) {
+    return make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                      pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
+}
+
+// Segment bounds clamped into [0, M]; an inverted pair is an empty segment.
+__device__ __forceinline__ void segment_rows(const int32_t *seg_start, int s, int M, int &lo,
+                                             int &hi) {
+    int a = seg_start[s];
+    int b = seg_start[s + 1];
+    a = a < 0 ? 0 : (a > M ? M : a);
+    b = b < 0 ? 0 : (b > M ? M : b);
+    lo = a;
+    hi = b < a ? a : b;
+}
+
+// Sum of NV values per lane across the 64 lanes of a wave, by recursive
+// halving: at each step a lane keeps half of its values and adds the
+// partner's copy of that half, so the shuffles shrink from NV to NV/2 to
+// ... 1, then plain butterflies finish the lane bits that remain. On return
+// vals[0] holds the wave-wide total of value index (lane >> (6 - log2 NV)).
+// Written as template recursion so every array index is a constant.
+template <int COUNT, int OFFSET>
+struct WaveHalving {
+    static __device__ __forceinline__ void run(float *vals, int lane) {
+        constexpr int half = COUNT / 2;
+        const bool upper = (lane & OFFSET) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = upper ? vals[i] : vals[i + half];
+            const float keep = upper ? vals[i + half] : vals[i];
+            vals[i] = keep + __shfl_xor(send, OFFSET, kWave);
+        }
+        WaveHalving<half, OFFSET / 2>::run(vals, lane);
+    }
+};
+
+template <int OFFSET>
+struct WaveHalving<1, OFFSET> {
+    static __device__ __forceinline__ void run(float *vals, int) {
+#pragma unroll
+        for (int o = OFFSET; o >= 1; o >>= 1) vals[0] += __shfl_xor(vals[0], o, kWave);
+    }
+};
+
+template <int NV>
+__device__ __forceinline__ void wave_reduce_transpose(float (&vals)[NV], int lane) {
+    static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of two <= 64");
+    WaveHalving<NV, 32>::run(vals, lane);
+}
+
+template <int NV>
+__host__ __device__ constexpr int log2_pow2() {
+    return NV <= 1 ? 0 : 1 + log2_pow2<NV / 2>();
+}
+
+}  // namespace sgmv

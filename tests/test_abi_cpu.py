@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, rejects bad arguments before enqueueing anything, and its host-side
+helpers (segment grouping, pool pointer table) are right. No compute call is
+made here: every call below returns during argument checks."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle as oracle_pkg
+import segmented_gather_gemm_sgmv_amd as sg
+
+from . import oracle_pins as pins
+from . import workloads as wl
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "sgmv.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(sgmv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(sg.EXPORTS)
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_symbol_exported(name):
+    assert hasattr(sg.lib, name)
+
+
+def test_status_strings():
+    for st in range(-8, 1):
+        assert sg.lib.sgmv_status_string(st)
+    assert sg.lib.sgmv_status_string(-99) == b"unknown status"
+
+
+# Distinct 256-byte aligned fake device addresses. They are never
+# dereferenced: each call below fails its argument checks (or is a no-op)
+# before anything is enqueued.
+P1, P2, P3, P4, P5, P6 = (0x100000 * (i + 1) for i in range(6))
+
+
+def shrink(V=P1, X=P2, A=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, r=16, dt=1):
+    return sg.lib.sgmv_shrink(V, X, A, P, ss, sa, N, M, d_in, r, dt, None)
+
+
+def expand(Y=P1, V=P2, B=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_out=64, r=16, alpha=32.0, dt=1):
+    return sg.lib.sgmv_expand(Y, V, B, P, ss, sa, N, M, d_out, r, alpha, dt, None)
+
+
+def fused(Y=P1, X=P2, A=P3, B=P6, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, d_out=64, r=16, dt=1,
+          ws=0x800000, wsb=1 << 20):
+    return sg.lib.sgmv_fused(Y, X, A, B, P, ss, sa, N, M, d_in, d_out, r, 32.0, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call", [shrink, expand, fused])
+def test_argument_errors(call):
+    assert call(r=12) == -3 and call(r=0) == -3 and call(r=128) == -3
+    assert call(dt=2) == -4 and call(dt=-1) == -4
+    assert call(M=-1) == -2 and call(N=-1) == -2 and call(P=-1) == -2
+    dim = "d_in" if call is not expand else "d_out"
+    assert call(**{dim: 12}) == -2 and call(**{dim: 0}) == -2
+    first = "V" if call is shrink else "Y"
+    assert call(**{first: None}) == -1
+    assert call(ss=None) == -1 and call(sa=None) == -1
+    assert call(**{first: P1 + 8}) == -5
+
+
+@pytest.mark.parametrize("call", [shrink, expand, fused])
+def test_empty_is_noop(call):
+    # nothing to do: OK without touching any pointer, even NULL ones
+    first = "V" if call is shrink else "Y"
+    assert call(M=0, **{first: None}) == 0
+    assert call(N=0, ss=None, sa=None) == 0
+
+
+def test_fused_workspace_checks():
+    need = sg.lib.sgmv_workspace_bytes(2, 4, 64, 64, 16, 1)
+    assert need >= 256 + 4 * 2 + 4 * 4 * 16
+    assert fused(ws=None) == -6
+    assert fused(wsb=need - 1) == -6
+    assert fused(ws=0x800000 + 16) == -6   # not 256-byte aligned
+    assert sg.lib.sgmv_workspace_bytes(2, 4, 64, 64, 12, 1) == 0
+
+
+def test_workspace_bytes_grows_with_rows():
+    a = sg.lib.sgmv_workspace_bytes(64, 64, 4096, 4096, 16, 1)
+    b = sg.lib.sgmv_workspace_bytes(64, 640, 4096, 4096, 16, 1)
+    assert b - a >= 576 * 16 * 4
+
+
+def test_build_segments_matches_oracle():
+    pins.pin_segments(sg.sgmv_build_segments)
+    rng = np.random.Generator(np.random.PCG64(30))
+    for _ in range(50):
+        ids = rng.integers(0, 9, size=int(rng.integers(0, 60))).astype(np.int32)
+        got = sg.sgmv_build_segments(ids)
+        want = oracle_pkg.build_segments(ids)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w)
+
+
+def test_build_segments_rejects_negative_ids():
+    with pytest.raises(sg.SGMVError):
+        sg.sgmv_build_segments([0, -1, 2])
+
+
+def test_pool_pointers_host():
+    table = np.zeros(5, np.uint64)
+    base = 0x7F0000000000
+    assert sg.lib.sgmv_pool_pointers(table.ctypes.data, base, 5, 4096) == 0
+    assert list(table) == [base + 4096 * k for k in range(5)]
+    assert sg.lib.sgmv_pool_pointers(table.ctypes.data, base, 5, 4100) == -5
+    assert sg.lib.sgmv_pool_pointers(table.ctypes.data, None, 5, 4096) == -1
+    assert sg.lib.sgmv_pool_pointers(None, None, 0, 4096) == 0
+
+
+def test_decode_skewed_segments_via_library():
+    w = wl.decode_skewed(sg.sgmv_build_segments)
+    _, ss, sa = oracle_pkg.build_segments(w.token_adapter)
+    assert np.array_equal(ss, w.seg_start) and np.array_equal(sa, w.seg_adapter)
+    assert w.M == 256 and w.seg_start[-1] == 256
+
+
+def test_pointer_table_keeps_pool_alive():
+    """A device pointer table must never outlive the pool it points into."""
+    import gc
+    import weakref
+
+    import torch
+    pool = torch.zeros((3, 8, 16), dtype=torch.bfloat16)
+    ref = weakref.ref(pool)
+    table = sg.sgmv_pool_pointers(pool)
+    assert table.tolist() == [pool.data_ptr() + k * 8 * 16 * 2 for k in range(3)]
+    del pool
+    gc.collect()
+    assert ref() is not None
+    del table
+    gc.collect()
+    assert ref() is None

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Bar: indexing (which rows receive which adapter) bit-exact; integer-valued
+inputs bit-exact; general inputs within |gpu - oracle| <= 1e-2 (1 + |oracle|)
+per element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as oracle_pkg
+import segmented_gather_gemm_sgmv_amd as sg
+
+from . import oracle_pins as pins
+from . import workloads as wl
+from .gpu_common import (TOL, assert_close, bits, oracle_bits, oracle_run, run_fused, run_split,
+                         to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def make_config(name):
+    if name == "tiny":
+        return wl.tiny()
+    if name == "decode_distinct":
+        return wl.decode_distinct()
+    if name == "decode_skewed":
+        return wl.decode_skewed(sg.sgmv_build_segments)
+    if name == "prefill":
+        return wl.prefill()
+    raise KeyError(name)
+
+
+CONFIGS = ["tiny", "decode_distinct", "decode_skewed", "prefill"]
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_config_parity(dev, oracle, name):
+    w = make_config(name)
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    V, Y = run_split(c)
+    ev = assert_close(V, V_ref, what=f"{name} shrink V")
+    ey = assert_close(Y, Y_ref, what=f"{name} shrink+expand Y")
+    Yf = run_fused(c)
+    ef = assert_close(Yf, Y_ref, what=f"{name} fused Y")
+    print(f"{name}: max rel err V {ev:.2e}  Y {ey:.2e}  fused {ef:.2e}")
+
+
+def _slice70b_rows(M, count=24):
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = set([0, M - 1]) | set(rng.choice(M, size=count - 2, replace=False).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+def test_slice70b_parity(dev, oracle):
+    """The 70B-layer slice at full size (512 rows, pools of 2000 adapters per
+    projection, 10.35 GB), checked on 24 sampled rows per projection."""
+    rows = _slice70b_rows(512)
+    for w in wl.slice70b():
+        A = wl.device_pool(w.num_adapters, w.r, w.d_in, w.d_in ** -0.5, w.seed + 1, dev)
+        B = wl.device_pool(w.num_adapters, w.r, w.d_out, w.r ** -0.5, w.seed + 2, dev)
+        c = to_device(w, dev, A_pool=A, B_pool=B)
+        V, Y = run_split(c)
+        Yf = run_fused(c)
+        # oracle on the sampled rows: each is its own segment; only their
+        # adapters' slots are copied back
+        ids = w.seg_adapter[rows]
+        sub = wl.Workload(w.name, len(rows), w.d_in, w.d_out, w.r, w.alpha, w.dtype, len(rows),
+                          wl.segments_from_lengths([1] * len(rows)), np.arange(len(rows), dtype=np.int32),
+                          X=w.X[torch.from_numpy(rows)], Y=w.Y[torch.from_numpy(rows)],
+                          A_pool=A[torch.from_numpy(ids).to(dev)].cpu(),
+                          B_pool=B[torch.from_numpy(ids).to(dev)].cpu())
+        V_ref, Y_ref = oracle_run(oracle, sub)
+        r_t = torch.from_numpy(rows).to(dev)
+        ev = assert_close(V[r_t], V_ref, what=f"{w.name} V")
+        ey = assert_close(Y[r_t], Y_ref, what=f"{w.name} Y")
+        ef = assert_close(Yf[r_t], Y_ref, what=f"{w.name} fused Y")
+        print(f"{w.name}: max rel err V {ev:.2e}  Y {ey:.2e}  fused {ef:.2e}")
+        del A, B, c
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_integer_exact(dev, oracle, name):
+    """Integer-valued inputs: every partial sum is exact, so the GPU must
+    match the oracle bit for bit, in either path, whatever its summation
+    order."""
+    w = wl.integer_case(np.random.Generator(np.random.PCG64(40)), make_config(name))
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    want = oracle_bits(oracle, Y_ref, w.dtype)
+    V, Y = run_split(c)
+    assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
+    assert np.array_equal(bits(Y), want)
+    assert np.array_equal(bits(run_fused(c)), want)
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+@pytest.mark.parametrize("mode", ["A", "B"])
+def test_indexing_signature(dev, oracle, name, mode):
+    """Each row's adapter id, written into the weights, must come back out
+    exactly, for the A fetch and the B fetch separately."""
+    w = make_config(name)
+    X, A, B, alpha = pins.signature_inputs(w.seg_start, w.seg_adapter, w.num_adapters,
+                                           w.d_in, w.d_out, w.r, mode, dtype=w.dtype)
+    w.X, w.A_pool, w.B_pool, w.alpha = X, A, B, alpha
+    w.Y = torch.zeros((w.M, w.d_out), dtype=w.dtype)
+    c = to_device(w, dev)
+    want = pins.row_adapter(w.seg_start, w.seg_adapter, w.M)
+    for Y in (run_split(c)[1], run_fused(c)):
+        y = Y.cpu().to(torch.float64).numpy()
+        assert np.array_equal(pins.decode_signature(y), want)
+        assert np.all(y[:, 4:] == 0)
+    # and the oracle agrees
+    _, Y_ref = oracle_run(oracle, w)
+    assert np.array_equal(pins.decode_signature(Y_ref), want)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("r", [8, 16, 32, 64])
+def test_random_small(dev, oracle, dtype, r):
+    """Ragged segments (empty ones included), repeated adapters, non-square
+    and ragged widths, nonzero Y, all ranks, both dtypes, both paths."""
+    rng = np.random.Generator(np.random.PCG64(50 + r + (dtype == torch.float32)))
+    for i in range(12):
+        w = wl.random_case(rng, dtype=dtype, max_M=40, max_seg=7, max_pool=6, ranks=(r,), max_d=600)
+        c = to_device(w, dev)
+        V_ref, Y_ref = oracle_run(oracle, w)
+        V, Y = run_split(c)
+        assert_close(V, V_ref, what=f"case {i} V")
+        assert_close(Y, Y_ref, what=f"case {i} Y")
+        assert_close(run_fused(c), Y_ref, what=f"case {i} fused")
+        wi = wl.integer_case(rng, w)
+        ci = to_device(wi, dev)
+        _, Yi_ref = oracle_run(oracle, wi)
+        want = oracle_bits(oracle, Yi_ref, dtype)
+        assert np.array_equal(bits(run_split(ci)[1]), want), f"case {i} integer split"
+        assert np.array_equal(bits(run_fused(ci)), want), f"case {i} integer fused"
+
+
+def test_long_segments_and_ragged_widths(dev, oracle):
+    """Segments longer than one register block (8 rows) and widths that end
+    inside a tile."""
+    rng = np.random.Generator(np.random.PCG64(60))
+    for dtype in (torch.bfloat16, torch.float32):
+        for d_in, d_out in [(8, 24), (4104, 520), (1032, 4104)]:
+            lengths = [37, 0, 9, 1, 100, 16, 17]
+            ids = rng.integers(0, 5, size=len(lengths)).astype(np.int32)
+            w = wl.Workload("long", int(sum(lengths)), d_in, d_out, 16, 32.0, dtype, 5,
+                            wl.segments_from_lengths(lengths), ids)
+            wl.fill_tensors(w, rng)
+            w.Y = wl._normal(rng, (w.M, w.d_out), 1.0, dtype)
+            c = to_device(w, dev)
+            V_ref, Y_ref = oracle_run(oracle, w)
+            V, Y = run_split(c)
+            assert_close(V, V_ref, what="V")
+            assert_close(Y, Y_ref, what="Y")
+            assert_close(run_fused(c), Y_ref, what="fused")
+
+
+def test_invalid_metadata_is_contained(dev, oracle):
+    """Adapter ids outside the pool skip their segment; segment bounds past
+    M are clamped. Nothing else changes."""
+    rng = np.random.Generator(np.random.PCG64(61))
+    w = wl.Workload("bad", 12, 64, 48, 8, 8.0, torch.bfloat16, 3,
+                    np.array([0, 3, 5, 9, 12], np.int32), np.array([1, -1, 3, 2], np.int32))
+    wl.fill_tensors(w, rng)
+    w.Y = wl._normal(rng, (w.M, w.d_out), 1.0, w.dtype)
+    c = to_device(w, dev)
+    # oracle on the valid segments only
+    ok = [0, 3]
+    ref_w = wl.Workload("ok", 12, 64, 48, 8, 8.0, torch.bfloat16, 3,
+                        np.array([0, 3, 9, 12], np.int32), np.array([1, 2, 2], np.int32),
+                        X=w.X, Y=w.Y, A_pool=w.A_pool, B_pool=w.B_pool)
+    _, Y_ref = oracle_run(oracle, ref_w)
+    for Y in (run_split(c)[1], run_fused(c)):
+        y = Y.cpu()
+        # rows 3..8 (adapter -1 and adapter 3 = P) untouched, bitwise
+        assert torch.equal(y[3:9], w.Y[3:9])
+        assert_close(Y[0:3], Y_ref[0:3])
+        assert_close(Y[9:12], Y_ref[9:12])
+    # bounds past M: [0, 4, 40] over M = 12 -> second segment is rows 4..11
+    w2 = wl.Workload("clamp", 12, 64, 48, 8, 8.0, torch.bfloat16, 3,
+                     np.array([0, 4, 40], np.int32), np.array([0, 2], np.int32),
+                     X=w.X, Y=w.Y, A_pool=w.A_pool, B_pool=w.B_pool)
+    c2 = to_device(w2, dev)
+    w2c = wl.Workload("clamped", 12, 64, 48, 8, 8.0, torch.bfloat16, 3,
+                      np.array([0, 4, 12], np.int32), np.array([0, 2], np.int32),
+                      X=w.X, Y=w.Y, A_pool=w.A_pool, B_pool=w.B_pool)
+    _, Y_ref2 = oracle_run(oracle, w2c)
+    assert_close(run_split(c2)[1], Y_ref2)
+    assert_close(run_fused(c2), Y_ref2)
+
+
+def test_empty_calls_are_noops(dev):
+    w = wl.tiny()
+    c = to_device(w, dev)
+    Y = c.Y0.clone() + 1
+    V = torch.full((w.M, w.r), 7.0, device=dev)
+    empty = torch.zeros(1, dtype=torch.int32, device=dev)
+    none = torch.zeros(0, dtype=torch.int32, device=dev)
+    sg.sgmv_shrink(V, c.X, c.A_ptrs, empty, none, w.r)
+    sg.sgmv_expand(Y, V, c.B_ptrs, empty, none, w.r, w.alpha)
+    sg.sgmv_fused(Y, c.X, c.A_ptrs, c.B_ptrs, empty, none, w.r, w.alpha)
+    torch.cuda.synchronize()
+    assert torch.all(V == 7.0) and torch.all(Y == 1.0)
+    X0 = torch.zeros((0, w.d_in), dtype=w.dtype, device=dev)
+    Y0 = torch.zeros((0, w.d_out), dtype=w.dtype, device=dev)
+    sg.sgmv_fused(Y0, X0, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
+    torch.cuda.synchronize()
+
+
+def test_guard_bands(dev, oracle):
+    """Sentinels before and after Y, V and the workspace survive every call."""
+    rng = np.random.Generator(np.random.PCG64(62))
+    w = wl.random_case(rng, dtype=torch.bfloat16, max_M=30, max_seg=5, ranks=(16,), max_d=300,
+                       allow_empty=False)
+    c = to_device(w, dev)
+    G = 4096
+    sentinel = -12345.0
+    Ybuf = torch.full((G + w.M * w.d_out + G,), sentinel, dtype=w.dtype, device=dev)
+    Vbuf = torch.full((G + w.M * w.r + G,), sentinel, dtype=torch.float32, device=dev)
+    Y = Ybuf[G:G + w.M * w.d_out].view(w.M, w.d_out)
+    V = Vbuf[G:G + w.M * w.r].view(w.M, w.r)
+    Y.copy_(c.Y0)
+    sg.sgmv_shrink(V, c.X, c.A_ptrs, c.seg_start, c.seg_adapter, w.r)
+    sg.sgmv_expand(Y, V, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
+    need = sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype)
+    WS = torch.zeros(256 + need + 4096, dtype=torch.uint8, device=dev)
+    WS[:256] = 0xA5
+    WS[256 + need:] = 0x5A
+    sg.sgmv_fused(Y, c.X, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha,
+                  workspace_buf=WS[256:256 + need])
+    torch.cuda.synchronize()
+    for buf, n in ((Ybuf, w.M * w.d_out), (Vbuf, w.M * w.r)):
+        assert torch.all(buf[:G] == sentinel) and torch.all(buf[G + n:] == sentinel)
+    assert torch.all(WS[:256] == 0xA5) and torch.all(WS[256 + need:] == 0x5A)
+    _, Y_ref = oracle_run(oracle, w)
+    # Y got the delta twice (split then fused)
+    Y_twice = oracle.expand(Y_ref, oracle.shrink(wl.storage(w.X), wl.storage(w.A_pool), w.seg_start,
+                                                 w.seg_adapter),
+                            wl.storage(w.B_pool), w.seg_start, w.seg_adapter, w.alpha)
+    assert_close(Y, Y_twice, tol=2 * TOL)
+
+
+def test_fused_workspace_reuse_and_reset(dev, oracle):
+    """The fused kernel leaves its control words at zero, so back-to-back
+    calls (the second smaller) share one workspace."""
+    rng = np.random.Generator(np.random.PCG64(63))
+    big = wl.random_case(rng, dtype=torch.bfloat16, max_M=40, max_seg=7, ranks=(16,), max_d=256)
+    small = wl.random_case(rng, dtype=torch.bfloat16, max_M=10, max_seg=3, ranks=(16,), max_d=256)
+    need = max(sg.sgmv_workspace_bytes(x.num_segments, x.M, x.d_in, x.d_out, x.r, x.dtype)
+               for x in (big, small))
+    WS = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for w in (big, small, big):
+        c = to_device(w, dev)
+        _, Y_ref = oracle_run(oracle, w)
+        assert_close(run_fused(c, workspace=WS), Y_ref)
+        ctl = WS[:256 + 4 * w.num_segments].view(torch.int32)
+        assert torch.all(ctl == 0), "control words not returned to zero"
+
+
+def test_deterministic(dev):
+    """Fixed-order reductions: repeated calls give identical bits."""
+    w = wl.decode_skewed(sg.sgmv_build_segments)
+    c = to_device(w, dev)
+    V1, Y1 = run_split(c)
+    V2, Y2 = run_split(c)
+    assert torch.equal(V1, V2) and torch.equal(Y1, Y2)
+    assert torch.equal(run_fused(c), run_fused(c))
+
+
+def test_fused_equals_split_bitwise_on_integers(dev):
+    w = wl.integer_case(np.random.Generator(np.random.PCG64(64)), wl.decode_distinct())
+    c = to_device(w, dev)
+    assert torch.equal(run_split(c)[1], run_fused(c))

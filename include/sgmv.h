@@ -110,10 +110,10 @@ int sgmv_expand(void *Y, const float *V, const uint64_t *B_ptrs, int32_t num_ada
  *
  * workspace: device memory of at least sgmv_workspace_bytes(...) bytes,
  * 256-byte aligned, zero-filled before its first use (for example by
- * hipMemset once after allocating it). Every call returns it to all-zero
- * control words when its kernel completes, so it can be reused by later calls
- * on the same stream without clearing. Calls that overlap in time (different
- * streams) must use different workspaces.
+ * hipMemset once after allocating it). Every call leaves the bytes it uses
+ * all zero again when its kernel completes, so one workspace serves any later
+ * call on the same stream, of any size that fits, without clearing. Calls
+ * that overlap in time (different streams) must use different workspaces.
  */
 int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
                int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,

@@ -7,6 +7,7 @@
 namespace sgmv {
 
 constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;  // threads per workgroup in every kernel (4 waves)
 
 // Storage element types. bf16 is kept as raw 16-bit patterns and widened by a
 // shift; fp32 is used as is.
@@ -19,23 +20,33 @@ struct Elem;
 template <>
 struct Elem<float> {
     static constexpr int kPerVec = 4;  // elements per 16-byte vector
+    static constexpr bool kIsBf16 = false;
 };
 template <>
 struct Elem<bf16_t> {
     static constexpr int kPerVec = 8;
+    static constexpr bool kIsBf16 = true;
 };
 
-// 16-byte vector load/store through the vector memory path.
-__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
-
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Global-memory (address space 1) views. Adapter pointers come out of a table
+// in memory and are generic; casting them here makes the compiler emit global
+// rather than flat loads.
+typedef __attribute__((address_space(1))) const u32x4_t gconst_vec_t;
+typedef __attribute__((address_space(1))) u32x4_t gvec_t;
+
+__device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// 16-byte loads and stores through the vector memory path.
+__device__ __forceinline__ uint4 ld16(const void *p) { return to_uint4(*(gconst_vec_t *)p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) {
+    *(gvec_t *)p = u32x4_t{v.x, v.y, v.z, v.w};
+}
 
 // Streaming load: weights are read once per call, so keep them out of the way
 // of data that is reused.
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    return to_uint4(__builtin_nontemporal_load((gconst_vec_t *)p));
 }
 
 // Widen one 16-byte vector to fp32 values.

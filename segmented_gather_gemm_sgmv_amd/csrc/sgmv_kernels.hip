@@ -13,63 +13,76 @@
 // across the segment's rows held in registers, so decode segments (a handful
 // of rows) run at the rate weights stream in from HBM.
 //
-//  * shrink: one workgroup per (segment, group of JG rank rows). The group's
-//    JG rows of A_k (stored r x d_in, each row contiguous) are streamed in
-//    16-byte loads spread over 256 lanes; each lane keeps partial dot products
-//    for every (row, rank) pair of the segment, which are then summed across
-//    the workgroup: a recursive-halving shuffle reduction inside each wave,
-//    then a fixed-order sum over the four waves in LDS. No atomics: the
-//    result is bitwise reproducible.
+//  * shrink: one wave per (segment, rank row j). Row j of A_k (stored r x
+//    d_in, each row contiguous) is streamed in 16-byte loads, eight in flight
+//    per lane; each lane keeps a partial dot product per segment row, and one
+//    recursive-halving shuffle reduction per wave finishes them. No LDS, no
+//    barrier, no atomics: results are bitwise reproducible.
 //  * expand: one workgroup per (segment, tile of d_out columns). B_k (stored
 //    r x d_out) is streamed row by row, 16 bytes per lane; V of the segment's
-//    rows is uniform across the workgroup; Y is read, updated in fp32 and
-//    rounded once on store.
-//  * fused: one launch whose workgroups take tickets from a counter: all
-//    shrink items come first, then all expand items. An expand item waits for
-//    its segment's shrink items; because those hold earlier tickets they were
-//    already claimed by running workgroups that never wait, so the wait always
-//    ends. The last workgroup to finish returns the counters to zero.
+//    rows is uniform across the workgroup and comes in through scalar loads; Y
+//    is read, updated in fp32 and rounded once on store.
+//  * fused: one launch; workgroups with the lowest ids do the shrink work,
+//    the rest the expand work. An expand workgroup waits for its segment's
+//    shrink workgroups, which have lower ids and so were dispatched first and
+//    never wait themselves. V passes between
+//    them through device-coherent (agent scope) stores and loads, published by
+//    a release increment of a per-segment arrival counter and picked up after
+//    an acquire; a second per-segment counter (departures) lets the segment's
+//    last expand workgroup return its counters and V rows to zero, so every
+//    launch leaves the whole workspace zero.
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
+#include "sgmv_mfma.h"
 
 namespace sgmv {
 
-constexpr int kShrinkThreads = 256;
-constexpr int kShrinkJG = 4;       // rank rows per shrink workgroup
-constexpr int kShrinkUnroll = 4;   // 16-byte vectors in flight per lane per rank row
-constexpr int kRowBlock = 8;       // rows held in registers at a time
-constexpr int kExpandThreads = 64;
+constexpr int kBlock = kBlockThreads;  // threads per workgroup (4 waves)
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kShrinkUnroll = 8;       // 16-byte A vectors in flight per lane
+constexpr int kRowBlock = 8;           // segment rows held in registers at a time
+
+// V written by one launch and read by another may use any cache; V handed
+// between workgroups of one launch uses device-coherent atomics.
+template <bool kCoherent>
+__device__ __forceinline__ void store_v(float *p, float v) {
+    if constexpr (kCoherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ float load_v(const float *p) {
+    if constexpr (kCoherent)
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return *p;
+}
+
+// Wait until every vector memory operation this wave issued has completed
+// (s_waitcnt with vmcnt = 0 and the other counters left alone).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ----------------------------------------------------------------------------
-// Shrink, one block of up to ROWS rows of one segment against JG rank rows.
+// Shrink: one wave, rank row j, up to ROWS rows of one segment.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int JG, int ROWS>
-__device__ __forceinline__ void shrink_rows(float *V, const T *__restrict__ X,
-                                            const T *__restrict__ Ak, int d_in, int row0,
-                                            int nrows, int j0, float (*red)[64]) {
+template <typename T, int R, int ROWS, bool kCoherent>
+__device__ __forceinline__ void shrink_wave(float *V, const T *X, const T *Arow, int d_in,
+                                            int row0, int nrows, int j, int lane) {
     constexpr int VEC = Elem<T>::kPerVec;
-    constexpr int NV = ROWS * JG;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const int nvec = d_in / VEC;
-
-    float acc[ROWS][JG];
+    float acc[ROWS];
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m)
-#pragma unroll
-        for (int jj = 0; jj < JG; ++jj) acc[m][jj] = 0.f;
+    for (int m = 0; m < ROWS; ++m) acc[m] = 0.f;
 
-    for (int base = 0; base < nvec; base += kShrinkThreads * kShrinkUnroll) {
-        uint4 a[kShrinkUnroll][JG];
+    for (int base = 0; base < nvec; base += kWave * kShrinkUnroll) {
+        uint4 a[kShrinkUnroll];
 #pragma unroll
         for (int u = 0; u < kShrinkUnroll; ++u) {
-            const int v = base + u * kShrinkThreads + tid;
-#pragma unroll
-            for (int jj = 0; jj < JG; ++jj)
-                a[u][jj] = v < nvec ? ld16_stream(Ak + (size_t)(j0 + jj) * d_in + (size_t)v * VEC)
-                                    : make_uint4(0, 0, 0, 0);
+            const int v = base + u * kWave + lane;
+            a[u] = v < nvec ? ld16_stream(Arow + (size_t)v * VEC) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int m = 0; m < ROWS; ++m) {
@@ -77,124 +90,131 @@ __device__ __forceinline__ void shrink_rows(float *V, const T *__restrict__ X,
                 const T *xrow = X + (size_t)(row0 + m) * d_in;
 #pragma unroll
                 for (int u = 0; u < kShrinkUnroll; ++u) {
-                    const int v = base + u * kShrinkThreads + tid;
+                    const int v = base + u * kWave + lane;
                     if (v < nvec) {
-                        float xf[VEC];
+                        float xf[VEC], af[VEC];
                         widen<T>(ld16(xrow + (size_t)v * VEC), xf);
+                        widen<T>(a[u], af);
 #pragma unroll
-                        for (int jj = 0; jj < JG; ++jj) {
-                            float af[VEC];
-                            widen<T>(a[u][jj], af);
-#pragma unroll
-                            for (int e = 0; e < VEC; ++e) acc[m][jj] = fmaf(xf[e], af[e], acc[m][jj]);
-                        }
+                        for (int e = 0; e < VEC; ++e) acc[m] = fmaf(xf[e], af[e], acc[m]);
                     }
                 }
             }
         }
     }
-
-    float vals[NV];
-#pragma unroll
-    for (int m = 0; m < ROWS; ++m)
-#pragma unroll
-        for (int jj = 0; jj < JG; ++jj) vals[m * JG + jj] = acc[m][jj];
-    wave_reduce_transpose<NV>(vals, lane);
-    constexpr int kSpread = kWave / NV;  // lanes that hold the same value index
-    if ((lane & (kSpread - 1)) == 0) red[wave][lane / kSpread] = vals[0];
-    __syncthreads();
-    if (tid < NV) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kShrinkThreads / kWave; ++w) sum += red[w][tid];
-        const int m = tid / JG;
-        const int jj = tid % JG;
-        if (m < nrows) V[(size_t)(row0 + m) * R + j0 + jj] = sum;
+    wave_reduce_transpose<ROWS>(acc, lane);
+    constexpr int kSpread = kWave / ROWS;  // lanes holding the same row's total
+    if ((lane & (kSpread - 1)) == 0) {
+        const int m = lane / kSpread;
+        if (m < nrows) store_v<kCoherent>(V + (size_t)(row0 + m) * R + j, acc[0]);
     }
-    __syncthreads();
 }
 
-// All rows of one segment for rank rows j0 .. j0+JG-1.
-template <typename T, int R, int JG>
-__device__ __forceinline__ void shrink_segment(float *V, const T *__restrict__ X,
-                                               const T *__restrict__ Ak, int d_in, int lo,
-                                               int hi, int j0, float (*red)[64]) {
+// All rows of one segment, rank row j, one wave.
+template <typename T, int R, bool kCoherent>
+__device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, const T *Arow, int d_in,
+                                                    int lo, int hi, int j, int lane) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            shrink_rows<T, R, JG, 1>(V, X, Ak, d_in, row0, nrows, j0, red);
+            shrink_wave<T, R, 1, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
         else if (nrows <= 2)
-            shrink_rows<T, R, JG, 2>(V, X, Ak, d_in, row0, nrows, j0, red);
+            shrink_wave<T, R, 2, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
         else if (nrows <= 4)
-            shrink_rows<T, R, JG, 4>(V, X, Ak, d_in, row0, nrows, j0, red);
+            shrink_wave<T, R, 4, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
         else
-            shrink_rows<T, R, JG, 8>(V, X, Ak, d_in, row0, nrows, j0, red);
+            shrink_wave<T, R, 8, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
     }
 }
 
+template <typename T>
+__device__ __forceinline__ bool takes_mfma(int rows) {
+    return Elem<T>::kIsBf16 && rows >= kLongRows;
+}
+
+// Items [0, N * R / 4): vector path, one per (segment, group of 4 rank rows),
+// skipping segments the MFMA path owns. Items after that: MFMA tiles of
+// kTileRows batch rows (bf16 only).
 template <typename T, int R>
-__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(
+__global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
-    const int32_t *__restrict__ seg_adapter, int M, int d_in) {
-    constexpr int JG = R < kShrinkJG ? R : kShrinkJG;
-    constexpr int groups = R / JG;
-    __shared__ float red[kShrinkThreads / kWave][64];
-    const int s = blockIdx.x / groups;
-    const int g = blockIdx.x % groups;
-    int lo, hi;
-    segment_rows(seg_start, s, M, lo, hi);
-    const int k = seg_adapter[s];
-    if (lo >= hi || k < 0 || k >= num_adapters) return;
-    const T *Ak = reinterpret_cast<const T *>(A_ptrs[k]);
-    shrink_segment<T, R, JG>(V, X, Ak, d_in, lo, hi, g * JG, red);
+    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in) {
+    constexpr int groups = R / kWavesPerBlock;
+    const int gemv_items = num_segments * groups;
+    if ((int)blockIdx.x < gemv_items) {
+        const int s = blockIdx.x / groups;
+        const int j = (blockIdx.x % groups) * kWavesPerBlock + (int)threadIdx.x / kWave;
+        const int lane = threadIdx.x & (kWave - 1);
+        int lo, hi;
+        segment_rows(seg_start, s, M, lo, hi);
+        const int k = seg_adapter[s];
+        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
+        const T *Arow = reinterpret_cast<const T *>(A_ptrs[k]) + (size_t)j * d_in;
+        shrink_segment_wave<T, R, false>(V, X, Arow, d_in, lo, hi, j, lane);
+        return;
+    }
+    if constexpr (Elem<T>::kIsBf16) {
+        __shared__ ShrinkSmem<R> sm;
+        __shared__ PieceList pl;
+        const int t0 = ((int)blockIdx.x - gemv_items) * kTileRows;
+        const int t1 = min(t0 + kTileRows, M);
+        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
+        for (int q = 0; q < pl.n; ++q) {
+            const Piece pc = pl.p[q];
+            const bf16_t *Ak = reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]);
+            shrink_piece_mfma<R, false>(reinterpret_cast<const bf16_t *>(X), Ak, d_in, t0, pc.lo,
+                                        pc.hi, sm, [&](size_t idx, float v) { V[idx] = v; });
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------
-// Expand, one block of up to RB rows of one segment, VEC columns per lane.
+// Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-// kCoherentV: V was written by other workgroups of this same launch (fused
-// path), so it is read with device-coherent vector loads; otherwise it came
-// from an earlier launch and may be read through any cache.
-template <bool kCoherentV>
-__device__ __forceinline__ float load_v(const float *p) {
-    if constexpr (kCoherentV)
-        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        return *p;
-}
-
-template <typename T, int R, int RB, bool kCoherentV>
-__device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *__restrict__ Bk,
-                                            int d_out, int row0, int nrows, int n0,
-                                            bool active, float scale) {
+template <typename T, int R, int RB, bool kCoherent>
+__device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, int d_out, int row0,
+                                            int nrows, int n0, bool active, float scale) {
     constexpr int VEC = Elem<T>::kPerVec;
-    constexpr int JC = R < 8 ? R : 8;  // rank rows of B held in registers at a time
+    constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     float acc[RB][VEC];
 #pragma unroll
     for (int m = 0; m < RB; ++m)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[m][e] = 0.f;
 
-    // Up to 16 rank rows are unrolled so all their loads are in flight at
-    // once; larger ranks stream 8 rows at a time to bound register use.
-    constexpr int kChunks = R <= 16 ? R / JC : 1;
-#pragma unroll kChunks
+#pragma unroll 1
     for (int jc = 0; jc < R; jc += JC) {
         uint4 b[JC];
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj)
             b[jj] = active ? ld16_stream(Bk + (size_t)(jc + jj) * d_out + n0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
-            float bf[VEC];
-            widen<T>(b[jj], bf);
+        for (int m = 0; m < RB; ++m) {
+            if (m < nrows) {
+                float v[JC];
+                if constexpr (kCoherent) {
 #pragma unroll
-            for (int m = 0; m < RB; ++m) {
-                if (m < nrows) {
-                    const float v = load_v<kCoherentV>(V + (size_t)(row0 + m) * R + jc + jj);
+                    for (int jj = 0; jj < JC; ++jj)
+                        v[jj] = load_v<true>(V + (size_t)(row0 + m) * R + jc + jj);
+                } else {
+                    // uniform across the workgroup: 16-byte scalar loads
+                    const float4 *vp = reinterpret_cast<const float4 *>(V + (size_t)(row0 + m) * R + jc);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[m][e] = fmaf(v, bf[e], acc[m][e]);
+                    for (int q = 0; q < JC / 4; ++q) {
+                        const float4 t = vp[q];
+                        v[4 * q] = t.x;
+                        v[4 * q + 1] = t.y;
+                        v[4 * q + 2] = t.z;
+                        v[4 * q + 3] = t.w;
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < JC; ++jj) {
+                    float bf[VEC];
+                    widen<T>(b[jj], bf);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[m][e] = fmaf(v[jj], bf[e], acc[m][e]);
                 }
             }
         }
@@ -213,131 +233,214 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *__res
     }
 }
 
-template <typename T, int R, bool kCoherentV>
-__device__ __forceinline__ void expand_segment(T *Y, const float *V, const T *__restrict__ Bk,
-                                               int d_out, int lo, int hi, int n0, bool active,
-                                               float scale) {
+template <typename T, int R, bool kCoherent>
+__device__ __forceinline__ void expand_segment(T *Y, const float *V, const T *Bk, int d_out, int lo,
+                                               int hi, int n0, bool active, float scale) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kCoherentV>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 1, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kCoherentV>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 2, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
         else if (nrows <= 4)
-            expand_rows<T, R, 4, kCoherentV>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 4, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
         else
-            expand_rows<T, R, 8, kCoherentV>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 8, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+    }
+}
+
+// Items [0, N * ntiles_g): vector path, one per (segment, tile of
+// kBlock * VEC columns; each wave takes kWave * VEC of them), skipping
+// segments the MFMA path owns. Items after that: MFMA tiles of kTileRows
+// batch rows by kExpandTileCols columns (bf16 only).
+template <typename T, int R>
+__global__ __launch_bounds__(kBlock) void expand_kernel(
+    T *__restrict__ Y, const float *__restrict__ V, const uint64_t *__restrict__ B_ptrs,
+    int num_adapters, const int32_t *__restrict__ seg_start,
+    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_out, int ntiles_g,
+    int ntiles_m, float scale) {
+    constexpr int VEC = Elem<T>::kPerVec;
+    const int gemv_items = num_segments * ntiles_g;
+    if ((int)blockIdx.x < gemv_items) {
+        const int s = blockIdx.x / ntiles_g;
+        const int tile = blockIdx.x % ntiles_g;
+        int lo, hi;
+        segment_rows(seg_start, s, M, lo, hi);
+        const int k = seg_adapter[s];
+        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
+        const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
+        const int n0 = (tile * kBlock + (int)threadIdx.x) * VEC;
+        expand_segment<T, R, false>(Y, V, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
+        return;
+    }
+    if constexpr (Elem<T>::kIsBf16) {
+        __shared__ ExpandSmem<R> sm;
+        __shared__ PieceList pl;
+        const int e = (int)blockIdx.x - gemv_items;
+        const int t0 = (e / ntiles_m) * kTileRows;
+        const int t1 = min(t0 + kTileRows, M);
+        const int n0 = (e % ntiles_m) * kExpandTileCols;
+        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
+        for (int q = 0; q < pl.n; ++q) {
+            const Piece pc = pl.p[q];
+            const bf16_t *Bk = reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]);
+            expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
+                                 sm, [&](size_t idx) { return V[idx]; });
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Fused: every shrink item (vector, then MFMA tiles) has a lower workgroup id
+// than every expand item (vector, then MFMA tiles).
+// ----------------------------------------------------------------------------
+
+// Thread 0 waits (bounded) until *counter reaches `target`, then acquires at
+// device scope. Returns 1 to every thread of the workgroup on success. The
+// producers hold lower workgroup ids, were dispatched earlier and never wait,
+// so the wait ends; the bound only guards against a workspace whose counters
+// were not zero on entry.
+__device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag) {
+    if (threadIdx.x == 0) {
+        uint32_t spins = 0;
+        int ok = 1;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > (1u << 26)) {
+                ok = 0;
+                break;
+            }
+        }
+        // no cache of this CU or XCD may serve V older than the count seen
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_flag = ok;
+    }
+    __syncthreads();
+    return *s_flag;
+}
+
+// Publish this workgroup's V stores: every wave waits for its stores, then
+// thread 0 increments the counter with release semantics at device scope.
+__device__ __forceinline__ void publish(uint32_t *counter) {
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this workgroup out; returns 1 to every thread if it was the last of
+// `expected` (all of them have finished reading V by then).
+__device__ __forceinline__ int depart_last(uint32_t *counter, uint32_t expected, int *s_flag) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == expected - 1;
+    }
+    __syncthreads();
+    return *s_flag;
+}
+
+__device__ __forceinline__ void zero_rows(float *Vws, int lo, int hi, int R) {
+    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock) store_v<true>(Vws + (size_t)lo * R + i, 0.f);
+}
+
+__device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 template <typename T, int R>
-__global__ __launch_bounds__(kExpandThreads) void expand_kernel(
-    T *__restrict__ Y, const float *__restrict__ V, const uint64_t *__restrict__ B_ptrs,
-    int num_adapters, const int32_t *__restrict__ seg_start,
-    const int32_t *__restrict__ seg_adapter, int M, int d_out, int ntiles, float scale) {
-    constexpr int VEC = Elem<T>::kPerVec;
-    const int s = blockIdx.x / ntiles;
-    const int tile = blockIdx.x % ntiles;
-    int lo, hi;
-    segment_rows(seg_start, s, M, lo, hi);
-    const int k = seg_adapter[s];
-    if (lo >= hi || k < 0 || k >= num_adapters) return;
-    const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
-    const int n0 = (tile * kExpandThreads + (int)threadIdx.x) * VEC;
-    expand_segment<T, R, false>(Y, V, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
-}
-
-// ----------------------------------------------------------------------------
-// Fused: shrink items, then expand items, ordered by tickets.
-// ----------------------------------------------------------------------------
-struct FusedControl {
-    uint32_t ticket;  // next item to hand out
-    uint32_t done;    // workgroups finished
-    uint32_t pad[62];
-};
-
-template <typename T, int R>
-__global__ __launch_bounds__(kShrinkThreads) void fused_kernel(
+__global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
-    int num_segments, int M, int d_in, int d_out, int ntiles, float scale,
-    FusedControl *ctl, uint32_t *ready, float *Vws) {
+    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
+    float scale, uint32_t *seg_arrive, uint32_t *seg_depart, uint32_t *tile_arrive,
+    uint32_t *tile_depart, float *Vws) {
     constexpr int VEC = Elem<T>::kPerVec;
-    constexpr int JG = R < kShrinkJG ? R : kShrinkJG;
-    constexpr int groups = R / JG;
-    __shared__ float red[kShrinkThreads / kWave][64];
-    __shared__ uint32_t s_item;
+    constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
-    const uint32_t shrink_items = (uint32_t)num_segments * groups;
-    const uint32_t total = gridDim.x;
+    const int item = blockIdx.x;
+    const int a0 = num_segments * groups;      // vector shrink items
+    const int a1 = a0 + num_tiles;             // MFMA shrink tiles
+    const int a2 = a1 + num_segments * ntiles_g;  // vector expand items; MFMA expand after
 
-    if (tid == 0) s_item = atomicAdd(&ctl->ticket, 1u);
-    __syncthreads();
-    const uint32_t item = s_item;
-
-    if (item < shrink_items) {
+    if (item < a0) {
         const int s = item / groups;
-        const int g = item % groups;
+        const int j = (item % groups) * kWavesPerBlock + tid / kWave;
         int lo, hi;
         segment_rows(seg_start, s, M, lo, hi);
         const int k = seg_adapter[s];
-        if (lo < hi && k >= 0 && k < num_adapters) {
-            const T *Ak = reinterpret_cast<const T *>(A_ptrs[k]);
-            shrink_segment<T, R, JG>(Vws, X, Ak, d_in, lo, hi, g * JG, red);
-            __threadfence();  // this lane's V stores are visible device-wide
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_fetch_add(&ready[s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else {
-        const uint32_t e = item - shrink_items;
-        const int s = e / ntiles;
-        const int tile = e % ntiles;
+        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
+        const T *Arow = reinterpret_cast<const T *>(A_ptrs[k]) + (size_t)j * d_in;
+        shrink_segment_wave<T, R, true>(Vws, X, Arow, d_in, lo, hi, j, tid & (kWave - 1));
+        publish(&seg_arrive[s]);
+        return;
+    }
+    if (item >= a1 && item < a2) {
+        const int e = item - a1;
+        const int s = e / ntiles_g;
+        const int tile = e % ntiles_g;
         int lo, hi;
         segment_rows(seg_start, s, M, lo, hi);
         const int k = seg_adapter[s];
-        if (lo < hi && k >= 0 && k < num_adapters) {
-            if (tid == 0) {
-                // Bounded wait: the producers hold earlier tickets and never
-                // wait, so this ends; the bound only guards against a broken
-                // workspace (counters not zero on entry).
-                uint32_t spins = 0;
-                int ok = 1;
-                while (__hip_atomic_load(&ready[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
-                       (uint32_t)groups) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > (1u << 26)) {
-                        ok = 0;
-                        break;
-                    }
-                }
-                s_flag = ok;
+        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
+        const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
+        const int n0 = (tile * kBlock + tid) * VEC;
+        if (wait_for(&seg_arrive[s], (uint32_t)groups, &s_flag))
+            expand_segment<T, R, true>(Y, Vws, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
+        if (depart_last(&seg_depart[s], (uint32_t)ntiles_g, &s_flag)) {
+            // last one out: return the segment's V rows and counters to zero
+            zero_rows(Vws, lo, hi, R);
+            reset_pair(&seg_arrive[s], &seg_depart[s]);
+        }
+        return;
+    }
+    if constexpr (Elem<T>::kIsBf16) {
+        __shared__ union {
+            ShrinkSmem<R> shrink;
+            ExpandSmem<R> expand;
+        } sm;
+        __shared__ PieceList pl;
+        const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
+        auto vstore = [&](size_t idx, float v) { store_v<true>(Vws + idx, v); };
+        auto vload = [&](size_t idx) { return load_v<true>(Vws + idx); };
+        if (item >= a0 && item < a1) {
+            const int t = item - a0;
+            const int t0 = t * kTileRows;
+            const int t1 = min(t0 + kTileRows, M);
+            gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
+            if (pl.n == 0) return;
+            for (int q = 0; q < pl.n; ++q) {
+                const Piece pc = pl.p[q];
+                shrink_piece_mfma<R, true>(Xb, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in,
+                                           t0, pc.lo, pc.hi, sm.shrink, vstore);
             }
-            __syncthreads();
-            __threadfence();
-            if (s_flag) {
-                const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
-                const int n0 = (tile * kShrinkThreads + tid) * VEC;
-                expand_segment<T, R, true>(Y, Vws, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
+            publish(&tile_arrive[t]);
+            return;
+        }
+        const int e = item - a2;
+        const int t = e / ntiles_m;
+        const int t0 = t * kTileRows;
+        const int t1 = min(t0 + kTileRows, M);
+        const int n0 = (e % ntiles_m) * kExpandTileCols;
+        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
+        if (pl.n == 0) return;
+        if (wait_for(&tile_arrive[t], 1u, &s_flag)) {
+            for (int q = 0; q < pl.n; ++q) {
+                const Piece pc = pl.p[q];
+                expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y),
+                                     reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]), d_out, t0, pc.lo,
+                                     pc.hi, n0, scale, sm.expand, vload);
             }
         }
-    }
-
-    // Retire: the last workgroup out returns the control words to zero.
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_flag = (prev == total - 1);
-    }
-    __syncthreads();
-    if (s_flag) {
-        for (int i = tid; i < num_segments; i += kShrinkThreads) ready[i] = 0;
-        if (tid == 0) {
-            ctl->ticket = 0;
-            ctl->done = 0;
+        if (depart_last(&tile_depart[t], (uint32_t)ntiles_m, &s_flag)) {
+            for (int q = 0; q < pl.n; ++q) zero_rows(Vws, pl.p[q].lo, pl.p[q].hi, R);
+            reset_pair(&tile_arrive[t], &tile_depart[t]);
         }
     }
 }
@@ -345,43 +448,54 @@ __global__ __launch_bounds__(kShrinkThreads) void fused_kernel(
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
+static_assert(kFusedTileRows == kTileRows, "fused workspace tiles must match the MFMA tiles");
+
+static int mfma_tiles(int dtype, int M) { return dtype == kBF16 ? (M + kTileRows - 1) / kTileRows : 0; }
+
+template <typename T>
+static int gemv_col_tiles(int d_out) {
+    const int cols = kBlock * Elem<T>::kPerVec;
+    return (d_out + cols - 1) / cols;
+}
+
 template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
-    constexpr int JG = R < kShrinkJG ? R : kShrinkJG;
-    const unsigned grid = (unsigned)a.num_segments * (R / JG);
-    hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kShrinkThreads), 0, st, a.V,
+    const unsigned grid =
+        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)mfma_tiles(a.dtype, a.M);
+    hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.M, a.d_in);
+                       a.seg_adapter, a.num_segments, a.M, a.d_in);
     return hipGetLastError();
 }
 
 template <typename T, int R>
 static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
-    constexpr int VEC = Elem<T>::kPerVec;
-    const int tile_cols = kExpandThreads * VEC;
-    const int ntiles = (a.d_out + tile_cols - 1) / tile_cols;
-    const unsigned grid = (unsigned)a.num_segments * ntiles;
-    hipLaunchKernelGGL((expand_kernel<T, R>), dim3(grid), dim3(kExpandThreads), 0, st,
+    const int ntiles_g = gemv_col_tiles<T>(a.d_out);
+    const int tiles = mfma_tiles(a.dtype, a.M);
+    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)tiles * ntiles_m;
+    hipLaunchKernelGGL((expand_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.M, a.d_out, ntiles, a.scale);
+                       a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
     return hipGetLastError();
 }
 
 template <typename T, int R>
 static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
-    constexpr int VEC = Elem<T>::kPerVec;
-    constexpr int JG = R < kShrinkJG ? R : kShrinkJG;
-    const int tile_cols = kShrinkThreads * VEC;
-    const int ntiles = (a.d_out + tile_cols - 1) / tile_cols;
-    const unsigned grid = (unsigned)a.num_segments * (R / JG) + (unsigned)a.num_segments * ntiles;
+    const int ntiles_g = gemv_col_tiles<T>(a.d_out);
+    const int tiles = mfma_tiles(a.dtype, a.M);
+    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const unsigned grid = (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)tiles +
+                          (unsigned)a.num_segments * ntiles_g + (unsigned)tiles * ntiles_m;
     const FusedLayout L = fused_layout(a.num_segments, a.M, a.r);
     char *ws = static_cast<char *>(a.workspace);
-    hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kShrinkThreads), 0, st,
+    uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
+    uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
+    hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles, a.scale,
-                       reinterpret_cast<FusedControl *>(ws + L.control),
-                       reinterpret_cast<uint32_t *>(ws + L.ready),
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, a.scale, seg_c,
+                       seg_c + a.num_segments, tile_c, tile_c + L.tiles,
                        reinterpret_cast<float *>(ws + L.v));
     return hipGetLastError();
 }

@@ -44,19 +44,24 @@ struct FusedArgs {
     void *workspace;
 };
 
-// Workspace of the fused kernel: a 256-byte control block (ticket and
-// retirement counters), one ready counter per segment, then V (M x r fp32).
+// Workspace of the fused kernel: two counters per segment (vector-path shrink
+// workgroups arrived, expand workgroups departed), two per MFMA row tile,
+// then V (M x r fp32). Every launch leaves all of it zero.
+constexpr int kFusedTileRows = 64;
+
 struct FusedLayout {
-    size_t control, ready, v, total;
+    size_t seg_counters, tile_counters, v, total;
+    int tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline FusedLayout fused_layout(int num_segments, int M, int r) {
     FusedLayout L;
-    L.control = 0;
-    L.ready = 256;
-    L.v = align256(L.ready + sizeof(uint32_t) * (size_t)num_segments);
+    L.tiles = (M + kFusedTileRows - 1) / kFusedTileRows;
+    L.seg_counters = 0;
+    L.tile_counters = 2 * sizeof(uint32_t) * (size_t)num_segments;
+    L.v = align256(L.tile_counters + 2 * sizeof(uint32_t) * (size_t)L.tiles);
     L.total = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
     return L;
 }

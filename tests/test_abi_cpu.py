@@ -80,7 +80,7 @@ def test_empty_is_noop(call):
 
 def test_fused_workspace_checks():
     need = sg.lib.sgmv_workspace_bytes(2, 4, 64, 64, 16, 1)
-    assert need >= 256 + 4 * 2 + 4 * 4 * 16
+    assert need >= 8 * 2 + 4 * 4 * 16
     assert fused(ws=None) == -6
     assert fused(wsb=need - 1) == -6
     assert fused(ws=0x800000 + 16) == -6   # not 256-byte aligned

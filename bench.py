@@ -105,7 +105,7 @@ def step(group, path, ws=None):
             sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
                           workspace_buf=ws)
         else:
-            sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r)
+            sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r, workspace_buf=ws)
             sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
 
 
@@ -134,37 +134,47 @@ def kernel_bytes(w, path):
     return {"shrink": x + a + v, "expand": b + y + v}
 
 
-def time_kernels(reps, path, steps, wsbuf):
-    """Average duration of each kernel of the path, from HIP events recorded
-    around every launch on the stream the kernels run on."""
-    import torch
+def launch_kernel(rp, name, ws=None):
     import segmented_gather_gemm_sgmv_amd as sg
-    stream = torch.cuda.current_stream()
+    w = rp.w
+    if name == "fused":
+        sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
+                      workspace_buf=ws)
+    elif name == "shrink":
+        sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r, workspace_buf=ws)
+    else:
+        sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
+
+
+def time_kernels(reps, path, steps, wsbuf):
+    """Average duration of each kernel of the path: a HIP graph holding only
+    that kernel, launched once per replica (and projection) in turn, replayed
+    until `steps` launches were timed, bracketed by HIP events recorded on the
+    replay stream."""
+    import torch
     names = ["fused"] if path == "fused" else ["shrink", "expand"]
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in names] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        group = reps[i % len(reps)]
-        for rp in group:
-            w = rp.w
-            if path == "fused":
-                evs[i][0][0].record(stream)
-                sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
-                              workspace_buf=wsbuf)
-                evs[i][0][1].record(stream)
-            else:
-                evs[i][0][0].record(stream)
-                sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r)
-                evs[i][0][1].record(stream)
-                evs[i][1][0].record(stream)
-                sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
-                evs[i][1][1].record(stream)
-    torch.cuda.synchronize()
+    R = len(reps)
     out = {}
-    for j, n in enumerate(names):
-        out[n] = float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
-    return out  # microseconds
+    for name in names:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for group in reps:
+                for rp in group:
+                    launch_kernel(rp, name, wsbuf)
+        g.replay()
+        torch.cuda.synchronize()
+        n_replays = max(1, steps // R)
+        stream = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_replays):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        launches = n_replays * sum(len(gr) for gr in reps)
+        out[name] = a.elapsed_time(b) * 1e3 / launches   # microseconds per launch
+        del g
+    return out
 
 
 def cpu_baseline(ws, seconds):
@@ -245,13 +255,14 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # per-kernel durations (events around each launch), for the roofline
-    kus = time_kernels(reps, args.path, min(args.steps, 1000), wsbuf)
+    # per-kernel durations, for the roofline
+    kus = time_kernels(reps, args.path, args.steps, wsbuf)
     per_kernel = kernel_bytes(ws[0], args.path)
-    if len(ws) > 1:  # several projections: sum their bytes per kernel name
+    if len(ws) > 1:  # several projections: average bytes per launch, as kus averages time
         for w in ws[1:]:
             for n, b in kernel_bytes(w, args.path).items():
                 per_kernel[n] += b
+        per_kernel = {n: b / len(ws) for n, b in per_kernel.items()}
     dom = max(kus, key=kus.get)   # the kernel that takes the most time per step
     achieved = per_kernel[dom] / (kus[dom] * 1e-6) / 1e9
 

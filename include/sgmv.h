@@ -86,10 +86,16 @@ enum sgmv_status {
  * V[m, j] = sum_i X[m, i] * A_k(i, j) for every row m of every segment.
  * V is overwritten for rows that lie in a segment with a valid adapter, and
  * left untouched elsewhere.
+ *
+ * workspace: as for sgmv_fused (same size query, same zero-filled contract).
+ * Long bf16 segments split the reduction over d_in between workgroups and
+ * combine the parts there, in a fixed order. May be NULL with
+ * workspace_bytes = 0 when sgmv_workspace_bytes(...) is 0.
  */
 int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
                 const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
-                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *stream);
+                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /*
  * Expand (same sources; the launch for all B, and the equation for y_i: the
@@ -121,7 +127,9 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
                float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
                void *stream);
 
-/* Bytes of workspace sgmv_fused needs for these sizes (0 on invalid sizes). */
+/* Bytes of workspace sgmv_shrink and sgmv_fused need for these sizes; one
+ * buffer of this size serves both (0 on invalid sizes, or when neither needs
+ * any). */
 size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
                             int32_t r, int32_t dtype);
 

@@ -31,7 +31,8 @@ _DTYPES = {torch.float32: SGMV_F32, torch.bfloat16: SGMV_BF16}
 # (name, restype, argtypes) for every symbol include/sgmv.h declares.
 _i32, _i64, _vp, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
 EXPORTS = {
-    "sgmv_shrink": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "sgmv_shrink": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                   _sz, _vp]),
     "sgmv_expand": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "sgmv_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _vp, _sz, _vp]),
@@ -94,17 +95,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
+def _workspace_args(t: Optional[torch.Tensor], need: int, like: torch.Tensor, stream):
+    if need == 0 and t is None:
+        return None, 0
+    if t is None:
+        t = workspace(like.device, need, stream)
+    return _dev(t, "workspace"), t.numel() * t.element_size()
+
+
 def sgmv_shrink(V: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, seg_start: torch.Tensor,
-                seg_adapter: torch.Tensor, r: int, stream=None) -> torch.Tensor:
+                seg_adapter: torch.Tensor, r: int, workspace_buf: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
     """V[M, r] (fp32, overwritten per segment row) = X[M, d_in] . A_k."""
     M, d_in = X.shape
     if V.shape != (M, r):
         raise ValueError("V must be M x r")
+    need = sgmv_workspace_bytes(seg_adapter.numel(), M, d_in, d_in, r, X.dtype)
+    ws, ws_bytes = _workspace_args(workspace_buf, need, X, stream)
     st = lib.sgmv_shrink(_dev(V, "V", torch.float32, 2), _dev(X, "X", dim=2),
                          _dev(A_ptrs, "A_ptrs", torch.int64, 1), A_ptrs.numel(),
                          _dev(seg_start, "seg_start", torch.int32, 1),
                          _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
-                         M, d_in, r, _dtype_code(X), _stream(X, stream))
+                         M, d_in, r, _dtype_code(X), ws, ws_bytes, _stream(X, stream))
     _check("sgmv_shrink", st)
     return V
 
@@ -133,9 +145,10 @@ _workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
 def workspace(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
-    """A zero-filled workspace for sgmv_fused, cached per (device, stream).
+    """A zero-filled workspace for sgmv_shrink and sgmv_fused, cached per
+    (device, stream).
 
-    The fused kernel returns its control words to zero when it completes, so
+    Every call leaves the workspace zero again when its kernel completes, so
     one buffer serves every later call on the same stream."""
     device = torch.device(device)
     key = (device.index if device.index is not None else torch.cuda.current_device(),
@@ -158,14 +171,12 @@ def sgmv_fused(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: t
     if A_ptrs.numel() != B_ptrs.numel():
         raise ValueError("A_ptrs and B_ptrs must have one entry per adapter")
     need = sgmv_workspace_bytes(seg_adapter.numel(), M, d_in, d_out, r, X.dtype)
-    if workspace_buf is None:
-        workspace_buf = workspace(X.device, need, stream)
+    ws, ws_bytes = _workspace_args(workspace_buf, need, X, stream)
     st = lib.sgmv_fused(_dev(Y, "Y", dim=2), _dev(X, "X", dim=2),
                         _dev(A_ptrs, "A_ptrs", torch.int64, 1), _dev(B_ptrs, "B_ptrs", torch.int64, 1),
                         A_ptrs.numel(), _dev(seg_start, "seg_start", torch.int32, 1),
                         _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
-                        M, d_in, d_out, r, float(alpha), _dtype_code(X),
-                        _dev(workspace_buf, "workspace"), workspace_buf.numel() * workspace_buf.element_size(),
+                        M, d_in, d_out, r, float(alpha), _dtype_code(X), ws, ws_bytes,
                         _stream(X, stream))
     _check("sgmv_fused", st)
     return Y

@@ -57,20 +57,33 @@ size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32
     if (num_segments < 0 || M < 0 || !valid_dim(d_in) || !valid_dim(d_out) || !valid_rank(r) ||
         !valid_dtype(dtype))
         return 0;
-    return sgmv::fused_layout(num_segments, M, r).total;
+    return std::max(sgmv::shrink_layout(M, d_in, r, dtype).total,
+                    sgmv::fused_layout(num_segments, M, d_in, r, dtype).total);
 }
+
+namespace {
+int check_workspace(const void *workspace, size_t workspace_bytes, size_t need) {
+    if (need == 0) return SGMV_OK;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+        return SGMV_ERR_WORKSPACE;
+    return SGMV_OK;
+}
+}  // namespace
 
 int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
                 const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
-                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *stream) {
+                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *workspace,
+                size_t workspace_bytes, void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
     if (!valid_dim(d_in) || (int64_t)M * d_in > kMaxElems) return SGMV_ERR_SHAPE;
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!V || !X || !A_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
     if (!aligned16(V) || !aligned16(X)) return SGMV_ERR_ALIGN;
+    st = check_workspace(workspace, workspace_bytes, sgmv::shrink_layout(M, d_in, r, dtype).total);
+    if (st != SGMV_OK) return st;
     sgmv::ShrinkArgs a{V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                       num_segments, M, d_in, r, dtype};
+                       num_segments, M, d_in, r, dtype, workspace};
     return hip_status(sgmv::launch_shrink(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -101,9 +114,9 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-        workspace_bytes < sgmv_workspace_bytes(num_segments, M, d_in, d_out, r, dtype))
-        return SGMV_ERR_WORKSPACE;
+    st = check_workspace(workspace, workspace_bytes,
+                         sgmv::fused_layout(num_segments, M, d_in, r, dtype).total);
+    if (st != SGMV_OK) return st;
     sgmv::FusedArgs a{Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
                       num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, workspace};
     return hip_status(sgmv::launch_fused(a, static_cast<hipStream_t>(stream)));

@@ -67,38 +67,53 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // ----------------------------------------------------------------------------
 // Shrink: one wave, rank row j, up to ROWS rows of one segment.
+//
+// Every load is unconditional: an address past the end of a row is clamped
+// back onto the row and its value masked to zero, and rows past the end of
+// the block repeat the last row and are simply not stored. Straight-line
+// loads let the compiler keep all of them in flight at once.
 // ----------------------------------------------------------------------------
 template <typename T, int R, int ROWS, bool kCoherent>
 __device__ __forceinline__ void shrink_wave(float *V, const T *X, const T *Arow, int d_in,
                                             int row0, int nrows, int j, int lane) {
     constexpr int VEC = Elem<T>::kPerVec;
+    constexpr int U = ROWS <= 2 ? kShrinkUnroll : (ROWS <= 4 ? kShrinkUnroll / 2 : kShrinkUnroll / 4);
     const int nvec = d_in / VEC;
     float acc[ROWS];
+    const T *xrow[ROWS];
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m) acc[m] = 0.f;
+    for (int m = 0; m < ROWS; ++m) {
+        acc[m] = 0.f;
+        xrow[m] = X + (size_t)(row0 + min(m, nrows - 1)) * d_in;
+    }
 
-    for (int base = 0; base < nvec; base += kWave * kShrinkUnroll) {
-        uint4 a[kShrinkUnroll];
+    for (int base = 0; base < nvec; base += kWave * U) {
+        uint4 a[U];
+        uint4 x[ROWS][U];
+        bool ok[U];
+        int vc[U];
 #pragma unroll
-        for (int u = 0; u < kShrinkUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int v = base + u * kWave + lane;
-            a[u] = v < nvec ? ld16_stream(Arow + (size_t)v * VEC) : make_uint4(0, 0, 0, 0);
+            ok[u] = v < nvec;
+            vc[u] = ok[u] ? v : nvec - 1;
+            a[u] = ld16_stream(Arow + (size_t)vc[u] * VEC);
         }
 #pragma unroll
-        for (int m = 0; m < ROWS; ++m) {
-            if (m < nrows) {
-                const T *xrow = X + (size_t)(row0 + m) * d_in;
+        for (int m = 0; m < ROWS; ++m)
 #pragma unroll
-                for (int u = 0; u < kShrinkUnroll; ++u) {
-                    const int v = base + u * kWave + lane;
-                    if (v < nvec) {
-                        float xf[VEC], af[VEC];
-                        widen<T>(ld16(xrow + (size_t)v * VEC), xf);
-                        widen<T>(a[u], af);
+            for (int u = 0; u < U; ++u) x[m][u] = ld16(xrow[m] + (size_t)vc[u] * VEC);
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[m] = fmaf(xf[e], af[e], acc[m]);
-                    }
-                }
+        for (int u = 0; u < U; ++u) {
+            if (!ok[u]) a[u] = make_uint4(0, 0, 0, 0);
+            float af[VEC];
+            widen<T>(a[u], af);
+#pragma unroll
+            for (int m = 0; m < ROWS; ++m) {
+                float xf[VEC];
+                widen<T>(x[m][u], xf);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[m] = fmaf(xf[e], af[e], acc[m]);
             }
         }
     }
@@ -132,14 +147,90 @@ __device__ __forceinline__ bool takes_mfma(int rows) {
     return Elem<T>::kIsBf16 && rows >= kLongRows;
 }
 
+// Count this workgroup in; returns 1 to every thread if it was the last of
+// `expected`. Acquire-release at device scope: the last one sees every
+// earlier workgroup's stores.
+__device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected, int *s_flag) {
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == expected - 1;
+    }
+    __syncthreads();
+    return *s_flag;
+}
+
+// One MFMA shrink item: part `kp` (of `ks`) of d_in for the 16-row tile `st`.
+// With ks == 1 the result goes straight to V; otherwise each part leaves its
+// 16 x R partial tile in the workspace and the last part to arrive sums the
+// parts in order 0 .. ks-1, writes V, and returns the partials and the
+// counter to zero. Returns 1 (to all threads) if V of this tile was written
+// by this workgroup, i.e. the tile is complete.
+template <int R, bool kCoherent>
+__device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptrs,
+                                const PieceList &pl, int d_in, int st, int kp, int ks,
+                                uint32_t *counters, float *partials, ShrinkSmem<R> &sm, int *s_flag) {
+    const int t0 = st * kShrinkTileRows;
+    const int nmacro = (d_in + kMacroK - 1) / kMacroK;
+    const int per = (nmacro + ks - 1) / ks;
+    const int ms0 = min(nmacro, kp * per);
+    const int ms1 = min(nmacro, ms0 + per);
+    float *part = partials + ((size_t)st * ks + kp) * kShrinkTileRows * R;
+    for (int q = 0; q < pl.n; ++q) {
+        const Piece pc = pl.p[q];
+        shrink_piece_mfma<R>(X, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in, t0, pc.lo, pc.hi,
+                             ms0, ms1, sm, [&](int m, int j, float v) {
+                                 if (ks == 1)
+                                     store_v<kCoherent>(V + (size_t)m * R + j, v);
+                                 else
+                                     store_v<true>(part + (m - t0) * R + j, v);
+                             });
+    }
+    if (ks == 1) return 1;
+    if (!arrive_last(&counters[st], (uint32_t)ks, s_flag)) return 0;
+    // Each thread owns at most R / 16 elements of the 16 x R tile; all their
+    // parts are loaded before any is summed or cleared, so the loads overlap.
+    constexpr int kPerThread = (kShrinkTileRows * R + kBlock - 1) / kBlock;
+    constexpr int kMaxParts = 16;
+    for (int q = 0; q < pl.n; ++q) {
+        const Piece pc = pl.p[q];
+        const int n = (pc.hi - pc.lo) * R;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            const int idx = threadIdx.x + e * kBlock;
+            if (idx < n) {
+                const int m = pc.lo + idx / R;
+                const size_t off = (size_t)(m - t0) * R + idx % R;
+                float part_v[kMaxParts];
+#pragma unroll
+                for (int k = 0; k < kMaxParts; ++k)
+                    if (k < ks) part_v[k] = load_v<true>(partials + ((size_t)st * ks + k) * kShrinkTileRows * R + off);
+                float sum = 0.f;
+#pragma unroll
+                for (int k = 0; k < kMaxParts; ++k)
+                    if (k < ks) sum += part_v[k];
+#pragma unroll
+                for (int k = 0; k < kMaxParts; ++k)
+                    if (k < ks) store_v<true>(partials + ((size_t)st * ks + k) * kShrinkTileRows * R + off, 0.f);
+                store_v<kCoherent>(V + (size_t)m * R + idx % R, sum);
+            }
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&counters[st], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 1;
+}
+
 // Items [0, N * R / 4): vector path, one per (segment, group of 4 rank rows),
-// skipping segments the MFMA path owns. Items after that: MFMA tiles of
-// kTileRows batch rows (bf16 only).
+// skipping segments the MFMA path owns. Items after that: MFMA shrink items,
+// one per (16-row tile, part of d_in) (bf16 only).
 template <typename T, int R>
 __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
-    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in) {
+    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int ks,
+    uint32_t *counters, float *partials) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = num_segments * groups;
     if ((int)blockIdx.x < gemv_items) {
@@ -157,15 +248,17 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
     if constexpr (Elem<T>::kIsBf16) {
         __shared__ ShrinkSmem<R> sm;
         __shared__ PieceList pl;
-        const int t0 = ((int)blockIdx.x - gemv_items) * kTileRows;
-        const int t1 = min(t0 + kTileRows, M);
-        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
-        for (int q = 0; q < pl.n; ++q) {
-            const Piece pc = pl.p[q];
-            const bf16_t *Ak = reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]);
-            shrink_piece_mfma<R, false>(reinterpret_cast<const bf16_t *>(X), Ak, d_in, t0, pc.lo,
-                                        pc.hi, sm, [&](size_t idx, float v) { V[idx] = v; });
-        }
+        __shared__ int s_flag;
+        const int subtiles = (M + kShrinkTileRows - 1) / kShrinkTileRows;
+        const int item = xcd_local_item(gemv_items, subtiles * ks);
+        if (item < 0) return;
+        const int st = item / ks;
+        const int t0 = st * kShrinkTileRows;
+        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
+                      min(t0 + kShrinkTileRows, M));
+        if (pl.n == 0) return;
+        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), A_ptrs, pl, d_in, st,
+                                   item % ks, ks, counters, partials, sm, &s_flag);
     }
 }
 
@@ -177,45 +270,49 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, i
                                             int nrows, int n0, bool active, float scale) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
+    // Loads are unconditional (see shrink_wave): an inactive lane reads
+    // column 0, rows past the block repeat the last row; neither is stored.
+    const int nc = active ? n0 : 0;
+    int rowc[RB];
+    uint4 yv[RB];
     float acc[RB][VEC];
 #pragma unroll
-    for (int m = 0; m < RB; ++m)
+    for (int m = 0; m < RB; ++m) {
+        rowc[m] = row0 + min(m, nrows - 1);
+        yv[m] = ld16(Y + (size_t)rowc[m] * d_out + nc);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[m][e] = 0.f;
+    }
 
 #pragma unroll 1
     for (int jc = 0; jc < R; jc += JC) {
         uint4 b[JC];
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj)
-            b[jj] = active ? ld16_stream(Bk + (size_t)(jc + jj) * d_out + n0) : make_uint4(0, 0, 0, 0);
+        for (int jj = 0; jj < JC; ++jj) b[jj] = ld16_stream(Bk + (size_t)(jc + jj) * d_out + nc);
 #pragma unroll
         for (int m = 0; m < RB; ++m) {
-            if (m < nrows) {
-                float v[JC];
-                if constexpr (kCoherent) {
+            float v[JC];
+            if constexpr (kCoherent) {
 #pragma unroll
-                    for (int jj = 0; jj < JC; ++jj)
-                        v[jj] = load_v<true>(V + (size_t)(row0 + m) * R + jc + jj);
-                } else {
-                    // uniform across the workgroup: 16-byte scalar loads
-                    const float4 *vp = reinterpret_cast<const float4 *>(V + (size_t)(row0 + m) * R + jc);
+                for (int jj = 0; jj < JC; ++jj) v[jj] = load_v<true>(V + (size_t)rowc[m] * R + jc + jj);
+            } else {
+                // uniform across the workgroup: 16-byte scalar loads
+                const float4 *vp = reinterpret_cast<const float4 *>(V + (size_t)rowc[m] * R + jc);
 #pragma unroll
-                    for (int q = 0; q < JC / 4; ++q) {
-                        const float4 t = vp[q];
-                        v[4 * q] = t.x;
-                        v[4 * q + 1] = t.y;
-                        v[4 * q + 2] = t.z;
-                        v[4 * q + 3] = t.w;
-                    }
+                for (int q = 0; q < JC / 4; ++q) {
+                    const float4 t = vp[q];
+                    v[4 * q] = t.x;
+                    v[4 * q + 1] = t.y;
+                    v[4 * q + 2] = t.z;
+                    v[4 * q + 3] = t.w;
                 }
+            }
 #pragma unroll
-                for (int jj = 0; jj < JC; ++jj) {
-                    float bf[VEC];
-                    widen<T>(b[jj], bf);
+            for (int jj = 0; jj < JC; ++jj) {
+                float bf[VEC];
+                widen<T>(b[jj], bf);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[m][e] = fmaf(v[jj], bf[e], acc[m][e]);
-                }
+                for (int e = 0; e < VEC; ++e) acc[m][e] = fmaf(v[jj], bf[e], acc[m][e]);
             }
         }
     }
@@ -223,12 +320,11 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, i
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
         if (m < nrows) {
-            T *yp = Y + (size_t)(row0 + m) * d_out + n0;
             float y[VEC];
-            widen<T>(ld16(yp), y);
+            widen<T>(yv[m], y);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] + scale * acc[m][e];
-            st16(yp, narrow<T>(y));
+            st16(Y + (size_t)(row0 + m) * d_out + n0, narrow<T>(y));
         }
     }
 }
@@ -276,7 +372,8 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
     if constexpr (Elem<T>::kIsBf16) {
         __shared__ ExpandSmem<R> sm;
         __shared__ PieceList pl;
-        const int e = (int)blockIdx.x - gemv_items;
+        const int e = xcd_local_item(gemv_items, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
+        if (e < 0) return;
         const int t0 = (e / ntiles_m) * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
@@ -357,17 +454,17 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
-    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    float scale, uint32_t *seg_arrive, uint32_t *seg_depart, uint32_t *tile_arrive,
-    uint32_t *tile_depart, float *Vws) {
+    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_subtiles,
+    int ks, float scale, uint32_t *seg_arrive, uint32_t *seg_depart, uint32_t *tile_arrive,
+    uint32_t *tile_depart, uint32_t *sub_arrive, float *Vws, float *partials) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
     const int item = blockIdx.x;
-    const int a0 = num_segments * groups;      // vector shrink items
-    const int a1 = a0 + num_tiles;             // MFMA shrink tiles
-    const int a2 = a1 + num_segments * ntiles_g;  // vector expand items; MFMA expand after
+    const int a0 = num_segments * groups;           // vector shrink items
+    const int a1 = a0 + round_up_xcds(num_subtiles * ks);  // MFMA shrink items (16 rows x part)
+    const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
     if (item < a0) {
         const int s = item / groups;
@@ -407,30 +504,38 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         } sm;
         __shared__ PieceList pl;
         const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
-        auto vstore = [&](size_t idx, float v) { store_v<true>(Vws + idx, v); };
         auto vload = [&](size_t idx) { return load_v<true>(Vws + idx); };
         if (item >= a0 && item < a1) {
-            const int t = item - a0;
-            const int t0 = t * kTileRows;
-            const int t1 = min(t0 + kTileRows, M);
-            gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
+            // (16-row tile, part of d_in); the workgroup that completes the
+            // tile reports to the arrival counter of its 64-row tile
+            const int it = xcd_local_item(a0, num_subtiles * ks);
+            if (it < 0) return;
+            const int st = it / ks;
+            const int t0 = st * kShrinkTileRows;
+            gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
+                          min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
-            for (int q = 0; q < pl.n; ++q) {
-                const Piece pc = pl.p[q];
-                shrink_piece_mfma<R, true>(Xb, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in,
-                                           t0, pc.lo, pc.hi, sm.shrink, vstore);
-            }
-            publish(&tile_arrive[t]);
+            if (shrink_mfma_item<R, true>(Vws, Xb, A_ptrs, pl, d_in, st, it % ks, ks, sub_arrive,
+                                          partials, sm.shrink, &s_flag))
+                publish(&tile_arrive[t0 / kTileRows]);
             return;
         }
-        const int e = item - a2;
+        const int e = xcd_local_item(a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
+        if (e < 0) return;
         const int t = e / ntiles_m;
         const int t0 = t * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
         if (pl.n == 0) return;
-        if (wait_for(&tile_arrive[t], 1u, &s_flag)) {
+        // one arrival per 16-row sub-tile that meets a long piece
+        uint32_t subtiles = 0;
+        for (int q0 = t0; q0 < t1; q0 += kShrinkTileRows) {
+            bool hit = false;
+            for (int q = 0; q < pl.n; ++q) hit |= pl.p[q].lo < q0 + kShrinkTileRows && pl.p[q].hi > q0;
+            subtiles += hit;
+        }
+        if (wait_for(&tile_arrive[t], subtiles, &s_flag)) {
             for (int q = 0; q < pl.n; ++q) {
                 const Piece pc = pl.p[q];
                 expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y),
@@ -448,9 +553,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
-static_assert(kFusedTileRows == kTileRows, "fused workspace tiles must match the MFMA tiles");
+static_assert(kTileRows64 == kTileRows && kSubTileRows == kShrinkTileRows && kMacroSteps == kMacroK,
+              "workspace layouts must match the MFMA tiles");
 
 static int mfma_tiles(int dtype, int M) { return dtype == kBF16 ? (M + kTileRows - 1) / kTileRows : 0; }
+
 
 template <typename T>
 static int gemv_col_tiles(int d_out) {
@@ -460,11 +567,15 @@ static int gemv_col_tiles(int d_out) {
 
 template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
+    const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const unsigned grid =
-        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)mfma_tiles(a.dtype, a.M);
+        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.subtiles * L.ks);
+    char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.num_segments, a.M, a.d_in);
+                       a.seg_adapter, a.num_segments, a.M, a.d_in, L.ks,
+                       L.ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
+                       L.ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr);
     return hipGetLastError();
 }
 
@@ -473,7 +584,7 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int tiles = mfma_tiles(a.dtype, a.M);
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
-    const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)tiles * ntiles_m;
+    const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     hipLaunchKernelGGL((expand_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
                        a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
@@ -482,21 +593,22 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
 
 template <typename T, int R>
 static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
+    const FusedLayout L = fused_layout(a.num_segments, a.M, a.d_in, a.r, a.dtype);
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
-    const int tiles = mfma_tiles(a.dtype, a.M);
-    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
-    const unsigned grid = (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)tiles +
-                          (unsigned)a.num_segments * ntiles_g + (unsigned)tiles * ntiles_m;
-    const FusedLayout L = fused_layout(a.num_segments, a.M, a.r);
+    const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const unsigned grid = (unsigned)a.num_segments * (R / kWavesPerBlock) +
+                          (unsigned)round_up_xcds(L.subtiles * L.ks) +
+                          (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(L.tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
     hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, a.scale, seg_c,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.subtiles, L.ks, a.scale, seg_c,
                        seg_c + a.num_segments, tile_c, tile_c + L.tiles,
-                       reinterpret_cast<float *>(ws + L.v));
+                       reinterpret_cast<uint32_t *>(ws + L.sub_counters),
+                       reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.partials));
     return hipGetLastError();
 }
 

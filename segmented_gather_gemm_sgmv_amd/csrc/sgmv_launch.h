@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace sgmv {
 
 enum DType { kF32 = 0, kBF16 = 1 };
@@ -18,6 +20,7 @@ struct ShrinkArgs {
     const int32_t *seg_start;
     const int32_t *seg_adapter;
     int num_segments, M, d_in, r, dtype;
+    void *workspace;
 };
 
 struct ExpandArgs {
@@ -44,25 +47,66 @@ struct FusedArgs {
     void *workspace;
 };
 
-// Workspace of the fused kernel: two counters per segment (vector-path shrink
-// workgroups arrived, expand workgroups departed), two per MFMA row tile,
-// then V (M x r fp32). Every launch leaves all of it zero.
-constexpr int kFusedTileRows = 64;
-
-struct FusedLayout {
-    size_t seg_counters, tile_counters, v, total;
-    int tiles;
-};
+constexpr int kSubTileRows = 16;   // rows of an MFMA shrink tile
+constexpr int kTileRows64 = 64;    // rows of an MFMA expand tile (and of a fused handoff)
+constexpr int kMacroSteps = 128;   // d_in elements per MFMA shrink macro step
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline FusedLayout fused_layout(int num_segments, int M, int r) {
+// How many workgroups split d_in for each 16-row MFMA shrink tile. One
+// workgroup streams only about 100 GB/s, so a batch with very few long rows
+// (at most 8 tiles of 16) spreads each tile over up to 4 workgroups, each
+// keeping at least four 128-wide macro steps per wave; larger batches
+// already have enough tiles to fill the chip and are not split.
+inline int shrink_ksplit(int M, int d_in) {
+    const int subtiles = (M + kSubTileRows - 1) / kSubTileRows;
+    const int nmacro = (d_in + kMacroSteps - 1) / kMacroSteps;
+    if (subtiles > 8) return 1;
+    return std::max(1, std::min(4, nmacro / 16));
+}
+
+// Shrink workspace (bf16 only, when the split is more than one part): one
+// arrival counter per 16-row tile, then the tiles' partial results
+// (tile x part x 16 x r fp32). Every launch leaves it all zero.
+struct ShrinkLayout {
+    size_t counters, partials, total;
+    int subtiles, ks;
+};
+
+inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
+    ShrinkLayout L;
+    L.subtiles = dtype == kBF16 ? (M + kSubTileRows - 1) / kSubTileRows : 0;
+    L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
+    L.counters = 0;
+    L.partials = align256(sizeof(uint32_t) * (size_t)L.subtiles);
+    L.total = L.ks > 1 ? align256(L.partials + sizeof(float) * (size_t)L.subtiles * L.ks *
+                                                   kSubTileRows * (size_t)r)
+                       : 0;
+    return L;
+}
+
+// Fused workspace: two counters per segment (vector-path shrink workgroups
+// arrived, expand workgroups departed), two per 64-row tile, one per 16-row
+// shrink tile, then V (M x r fp32), then the split partials as above. Every
+// launch leaves it all zero.
+struct FusedLayout {
+    size_t seg_counters, tile_counters, sub_counters, v, partials, total;
+    int tiles, subtiles, ks;
+};
+
+inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dtype) {
     FusedLayout L;
-    L.tiles = (M + kFusedTileRows - 1) / kFusedTileRows;
+    L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
+    L.subtiles = dtype == kBF16 ? (M + kSubTileRows - 1) / kSubTileRows : 0;
+    L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.seg_counters = 0;
     L.tile_counters = 2 * sizeof(uint32_t) * (size_t)num_segments;
-    L.v = align256(L.tile_counters + 2 * sizeof(uint32_t) * (size_t)L.tiles);
-    L.total = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
+    L.sub_counters = L.tile_counters + 2 * sizeof(uint32_t) * (size_t)L.tiles;
+    L.v = align256(L.sub_counters + sizeof(uint32_t) * (size_t)L.subtiles);
+    L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
+    L.total = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.subtiles * L.ks *
+                                                    kSubTileRows * (size_t)r
+                                              : 0));
     return L;
 }
 

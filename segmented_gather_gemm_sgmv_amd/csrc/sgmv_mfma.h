@@ -14,10 +14,10 @@
 // consecutive elements of the reduction dimension as long as its A and B
 // operands agree on which ones.
 //
-//  * shrink piece: D = X_rows (16 x d_in) . A_k^T (d_in x r). X rows are
-//    read straight from HBM into the A operand; A_k is staged through LDS in
-//    chunks of kShrinkKStep columns (double-buffered) and shared by the four
-//    waves. fp32 accumulation.
+//  * shrink piece: D = X_rows (16 x d_in) . A_k^T (d_in x r) on 16-row
+//    tiles, the reduction split over the four waves; both operands go
+//    straight from HBM into registers, two macro steps in flight per lane.
+//    fp32 accumulation.
 //  * expand piece: D = V_rows (16 x r) . B_k (r x 128 columns). V is fp32 and
 //    enters the A operand as two bf16 halves, hi = rne(v) and lo = rne(v - hi),
 //    so hi + lo carries 16 significant bits; both halves meet the same B
@@ -35,7 +35,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kLongRows = 16;           // segments this long or longer take the MFMA path
 constexpr int kTileRows = 64;           // batch rows per MFMA tile (4 waves x 16)
-constexpr int kShrinkKStep = 64;        // d_in elements staged per chunk
 constexpr int kExpandTileCols = 128;    // d_out columns per expand tile
 constexpr int kMaxPieces = 8;           // long segments one window of a tile can meet
 
@@ -43,6 +42,21 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroups are dealt to the 8 XCDs of the chip round-robin by id, and each
+// XCD has its own L2. Remap a run of `count` MFMA items (the first at
+// workgroup id `first_id`) so that each XCD gets a contiguous block of item
+// indices: consecutive row tiles belong to the same segments and re-read the
+// same adapter, which then stays in one L2. Returns -1 for the padding ids
+// (the run is launched rounded up to a multiple of 8).
+constexpr int kXcds = 8;
+__host__ __device__ constexpr int round_up_xcds(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
+__device__ __forceinline__ int xcd_local_item(int first_id, int count) {
+    const int j = (int)blockIdx.x - first_id;
+    const int per = (count + kXcds - 1) / kXcds;
+    const int item = ((int)blockIdx.x % kXcds) * per + j / kXcds;
+    return item < count ? item : -1;
 }
 
 __device__ __forceinline__ int clamp_to(int v, int M) { return v < 0 ? 0 : (v > M ? M : v); }
@@ -76,19 +90,44 @@ struct Piece {
 struct PieceList {
     Piece p[kMaxPieces];
     int n;
-    int starts[kWave + 1];
     int more, next;
+    int starts[kBlockThreads + 1];
+    int ids[kBlockThreads];
 };
 
+__device__ __forceinline__ void consider_segment(PieceList &pl, int s, int lo, int hi, int k,
+                                                 int num_adapters, int t0, int t1) {
+    if (hi - lo >= kLongRows && lo < t1 && hi > t0 && k >= 0 && k < num_adapters) {
+        const int slot = atomicAdd(&pl.n, 1);
+        if (slot < kMaxPieces) pl.p[slot] = Piece{max(lo, t0), min(hi, t1), s, k};
+    }
+}
+
 // Collect into `pl` the long segments (with a valid adapter) that intersect
-// rows [t0, t1) of the batch. Offsets are scanned in windows of kWave
-// segments from the one holding row t0, until a segment starts at or past
-// t1. With valid (non-decreasing) offsets at most five long segments meet a
-// tile; pieces beyond kMaxPieces (possible only with invalid offsets) are
-// dropped. Call with the whole workgroup; pl is visible to all on return.
+// rows [t0, t1) of the batch. With up to kBlockThreads - 1 segments all the
+// offsets and ids come in with one load per thread. Otherwise the segment
+// holding row t0 is found by a k-ary search and the offsets are scanned in
+// windows of kWave segments until one starts at or past t1. With valid
+// (non-decreasing) offsets at most five long segments meet a tile; pieces
+// beyond kMaxPieces (possible only with invalid offsets) are dropped. Call
+// with the whole workgroup; pl is visible to all threads on return.
 __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int32_t *seg_adapter,
                               int num_segments, int num_adapters, int M, int t0, int t1) {
     const int tid = threadIdx.x;
+    if (num_segments < kBlockThreads) {
+        if (tid == 0) pl.n = 0;
+        if (tid <= num_segments) pl.starts[tid] = clamp_to(seg_start[tid], M);
+        if (tid < num_segments) pl.ids[tid] = seg_adapter[tid];
+        __syncthreads();
+        if (tid < num_segments) {
+            const int lo = pl.starts[tid];
+            consider_segment(pl, tid, lo, max(lo, pl.starts[tid + 1]), pl.ids[tid], num_adapters, t0, t1);
+        }
+        __syncthreads();
+        if (tid == 0 && pl.n > kMaxPieces) pl.n = kMaxPieces;
+        __syncthreads();
+        return;
+    }
     const int cnt = count_starts_le<kBlockThreads>(seg_start, num_segments, M, t0);
     int first = cnt > 0 ? cnt - 1 : 0;
     if (tid == 0) pl.n = 0;
@@ -103,13 +142,8 @@ __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int
             if (s < num_segments) {
                 const int lo = pl.starts[tid];
                 const int hi = max(lo, pl.starts[tid + 1]);
-                if (hi - lo >= kLongRows && lo < t1 && hi > t0) {
-                    const int k = seg_adapter[s];
-                    if (k >= 0 && k < num_adapters) {
-                        const int slot = atomicAdd(&pl.n, 1);
-                        if (slot < kMaxPieces) pl.p[slot] = Piece{max(lo, t0), min(hi, t1), s, k};
-                    }
-                }
+                if (hi - lo >= kLongRows && lo < t1 && hi > t0)
+                    consider_segment(pl, s, lo, hi, seg_adapter[s], num_adapters, t0, t1);
             }
         }
         if (tid == 0) {
@@ -127,109 +161,121 @@ __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int
 }
 
 // ----------------------------------------------------------------------------
-// Shrink piece: V[m, 0:R] = X[m, :] . A_k for rows m in [p0, p1) of tile t0.
+// Shrink piece: V[m, 0:R] = X[m, :] . A_k for rows m in [p0, p1) of the
+// 16-row tile starting at t0. The four waves split d_in: wave w takes macro
+// steps w, w+4, ... of kMacroK elements. In a macro step lane (i, g) brings,
+// for each of four MFMA k-slices q, elements kb + 32 q + 8 g .. +7 of X row i
+// and of A_k rows 16 b + i (b < NB), so the four lanes of a row read 64
+// contiguous bytes per instruction. kDepth macro steps are in flight per
+// lane. X rows are read once (streaming loads); A_k is re-read by every tile
+// of its segment and kept in cache. The waves' partial 16 x R tiles are
+// summed in LDS in a fixed order.
 // ----------------------------------------------------------------------------
+constexpr int kShrinkTileRows = 16;
+constexpr int kMacroK = 128;
+
 template <int R>
 struct ShrinkSmem {
     static constexpr int kNB = R < 16 ? 1 : R / 16;            // 16-column MFMA blocks
-    static constexpr int kRows = kNB * 16;                       // staged rows (zero past R)
-    static constexpr int kStride = kShrinkKStep + 8;             // bf16 per staged row (padded)
-    uint16_t a[2][kRows * kStride];
+    static constexpr int kCols = kNB * 16;
+    float red[kBlockThreads / kWave][16 * kCols];
 };
 
-template <int R, bool kCoherent, typename StoreV>
+template <int NB>
+struct ShrinkOperands {
+    uint4 x[4];
+    uint4 a[NB][4];
+    uint32_t ok;  // bit q: slice q lies inside d_in
+};
+
+template <int R, typename StoreV>
 __device__ void shrink_piece_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int p0, int p1,
-                                  ShrinkSmem<R> &sm, StoreV store_v_fn) {
+                                  int ms_begin, int ms_end, ShrinkSmem<R> &sm, StoreV store_v_fn) {
     constexpr int NB = ShrinkSmem<R>::kNB;
-    constexpr int kStride = ShrinkSmem<R>::kStride;
-    constexpr int kChunkVecs = R * (kShrinkKStep / 8);          // 16-byte vectors per chunk
-    constexpr int kPer = (kChunkVecs + kBlockThreads - 1) / kBlockThreads;
+    constexpr int kCols = ShrinkSmem<R>::kCols;
+    constexpr int kWaves = kBlockThreads / kWave;
+    constexpr int kDepth = NB == 1 ? 4 : (NB == 2 ? 3 : 2);      // macro steps in flight
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int g = lane >> 4;
     const int i = lane & 15;
-    const int row = t0 + 16 * wave + i;
+    const int row = t0 + i;
     const bool row_ok = row >= p0 && row < p1;
-    const bf16_t *xrow = X + (size_t)(row_ok ? row : p0) * d_in;
-    const int nsteps = (d_in + kShrinkKStep - 1) / kShrinkKStep;
+    const bf16_t *xrow = X + (size_t)(row_ok ? row : p0) * d_in;  // others: never stored
+    // This piece covers macro steps [ms_begin, ms_end) of d_in. Every wave
+    // runs the same number of steps, padded to a multiple of kDepth; a step
+    // past the end loads clamped addresses and zeroes its X, so loads never
+    // sit behind a branch and all kDepth steps stay in flight.
+    const int nper = (ms_end - ms_begin + kWaves - 1) / kWaves;
+    const int niter = (nper + kDepth - 1) / kDepth * kDepth;
 
-    // Staged rows past R (only when R < 16) stay zero for the whole piece.
-    if (R < 16) {
-        for (int idx = tid; idx < 2 * (NB * 16 - R) * kStride; idx += kBlockThreads) {
-            const int b = idx / ((NB * 16 - R) * kStride);
-            const int rem = idx % ((NB * 16 - R) * kStride);
-            sm.a[b][R * kStride + rem] = 0;
-        }
-    }
-
-    uint4 creg[kPer];
-    uint4 xcur[2], xnext[2];
-    auto load_chunk = [&](int step) {
+    // A slice outside the piece's range loads from a clamped address; its X is
+    // replaced by zero when the MFMA operand is formed (never by writing over
+    // the load's destination, which would make the load wait).
+    auto load = [&](ShrinkOperands<NB> &op, int it) {
+        const int ms = ms_begin + wave + it * kWaves;
+        const int kb = ms * kMacroK + 8 * g;
+        op.ok = 0;
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int idx = tid + q * kBlockThreads;
-            const int j = idx >> 3;
-            const int k = step * kShrinkKStep + (idx & 7) * 8;
-            creg[q] = (idx < kChunkVecs && k < d_in) ? ld16_stream(Ak + (size_t)j * d_in + k)
-                                                     : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_chunk = [&](int buf) {
+        for (int q = 0; q < 4; ++q) {
+            const int k = kb + 32 * q;
+            const bool ok = ms < ms_end && k < d_in;
+            const int kc = ok ? k : d_in - 8;
+            op.ok |= (uint32_t)ok << q;
+            op.x[q] = ld16_stream(xrow + kc);
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int idx = tid + q * kBlockThreads;
-            if (idx < kChunkVecs)
-                *reinterpret_cast<uint4 *>(&sm.a[buf][(idx >> 3) * kStride + (idx & 7) * 8]) = creg[q];
+            for (int b = 0; b < NB; ++b) {
+                const int j = min(16 * b + i, R - 1);  // columns past R are never stored
+                op.a[b][q] = ld16(Ak + (size_t)j * d_in + kc);
+            }
         }
     };
-    auto load_x = [&](int step, uint4 (&xr)[2]) {
-        const int k = step * kShrinkKStep + 16 * g;
-        xr[0] = (row_ok && k < d_in) ? ld16(xrow + k) : make_uint4(0, 0, 0, 0);
-        xr[1] = (row_ok && k + 8 < d_in) ? ld16(xrow + k + 8) : make_uint4(0, 0, 0, 0);
-    };
-
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_chunk(0);
-    load_x(0, xcur);
-    store_chunk(0);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        const bool more = st + 1 < nsteps;
-        if (more) {
-            load_chunk(st + 1);
-            load_x(st + 1, xnext);
-        }
+    // The memory counter retires loads in issue order, so each group of loads
+    // must stay where it is written: scheduling barriers stop the compiler
+    // from interleaving the groups, and consuming the oldest group then waits
+    // only for that group.
+    ShrinkOperands<NB> buf[kDepth];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bf16x8_t a = as_bf16x8(xcur[h]);
+    for (int u = 0; u < kDepth - 1; ++u) {
+        load(buf[u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int it0 = 0; it0 < niter; it0 += kDepth) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint4 bv = *reinterpret_cast<const uint4 *>(
-                    &sm.a[buf][(16 * b + i) * kStride + 16 * g + 8 * h]);
-                acc[b] = mfma_bf16(a, as_bf16x8(bv), acc[b]);
+        for (int u = 0; u < kDepth; ++u) {
+            load(buf[(u + kDepth - 1) % kDepth], it0 + u + kDepth - 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 xq = ((buf[u].ok >> q) & 1u) ? buf[u].x[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = mfma_bf16(as_bf16x8(xq), as_bf16x8(buf[u].a[b][q]), acc[b]);
             }
-        }
-        if (more) {
-            store_chunk(buf ^ 1);
-            xcur[0] = xnext[0];
-            xcur[1] = xnext[1];
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = t0 + 16 * wave + 4 * g + v;
-            const int j = 16 * b + i;
-            if (m >= p0 && m < p1 && j < R) store_v_fn((size_t)m * R + j, acc[b][v]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+
+    // fixed-order sum of the four waves' partial tiles
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.red[wave][(4 * g + v) * kCols + 16 * b + i] = acc[b][v];
+    __syncthreads();
+    for (int idx = tid; idx < 16 * R; idx += kBlockThreads) {
+        const int m = idx / R;
+        const int j = idx % R;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += sm.red[w][m * kCols + j];
+        if (t0 + m >= p0 && t0 + m < p1) store_v_fn(t0 + m, j, sum);
+    }
+    __syncthreads();
 }
 
 // ----------------------------------------------------------------------------
@@ -271,19 +317,17 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
         const int idx = tid + q * kBlockThreads;
         const int m = t0 + idx / kColVecs;
         const int n = n0 + (idx % kColVecs) * 8;
-        yv[q] = (m >= p0 && m < p1 && n < d_out) ? ld16(Y + (size_t)m * d_out + n) : make_uint4(0, 0, 0, 0);
+        const bool ok = m >= p0 && m < p1 && n < d_out;
+        yv[q] = ld16(Y + (size_t)(ok ? m : p0) * d_out + (ok ? n : 0));  // others: never stored
     }
 
     // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
     for (int idx = tid; idx < (R / 2) * kColVecs; idx += kBlockThreads) {
         const int jp = idx / kColVecs;
         const int c8 = idx % kColVecs;
-        const int n = n0 + c8 * 8;
-        uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
-        if (n < d_out) {
-            r0 = ld16_stream(Bk + (size_t)(2 * jp) * d_out + n);
-            r1 = ld16_stream(Bk + (size_t)(2 * jp + 1) * d_out + n);
-        }
+        const int n = n0 + c8 * 8 < d_out ? n0 + c8 * 8 : 0;  // columns past d_out are never stored
+        const uint4 r0 = ld16(Bk + (size_t)(2 * jp) * d_out + n);
+        const uint4 r1 = ld16(Bk + (size_t)(2 * jp + 1) * d_out + n);
         const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
         const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
@@ -293,7 +337,7 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
             *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
         }
     }
-    if (R < K) {  // zero the padded part of the reduction
+    if constexpr (R < K) {  // zero the padded part of the reduction
         for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
             sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
     }
@@ -310,8 +354,12 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
             float v2[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                // rows outside the piece are never stored; rank columns past R
+                // meet zero rows of the staged B tile but are zeroed anyway so
+                // a non-finite value cannot leak into a valid row
                 const int j = ks * 32 + 8 * g + 2 * e2 + u;
-                v2[u] = (row_ok && j < R) ? load_v_fn((size_t)row * R + j) : 0.f;
+                const float v = load_v_fn((size_t)(row_ok ? row : p0) * R + min(j, R - 1));
+                v2[u] = j < R ? v : 0.f;
             }
             const uint32_t hb0 = bf16_bits(v2[0]), hb1 = bf16_bits(v2[1]);
             const float r0 = v2[0] - __uint_as_float(hb0 << 16);

@@ -39,10 +39,10 @@ def to_device(w: wl.Workload, dev, A_pool=None, B_pool=None) -> DeviceCase:
         seg_adapter=torch.from_numpy(np.ascontiguousarray(w.seg_adapter, np.int32)).to(dev))
 
 
-def run_split(c: DeviceCase, Y=None):
+def run_split(c: DeviceCase, Y=None, workspace=None):
     V = torch.zeros((c.w.M, c.w.r), dtype=torch.float32, device=c.X.device)
     Y = c.Y0.clone() if Y is None else Y
-    sg.sgmv_shrink(V, c.X, c.A_ptrs, c.seg_start, c.seg_adapter, c.w.r)
+    sg.sgmv_shrink(V, c.X, c.A_ptrs, c.seg_start, c.seg_adapter, c.w.r, workspace_buf=workspace)
     sg.sgmv_expand(Y, V, c.B_ptrs, c.seg_start, c.seg_adapter, c.w.r, c.w.alpha)
     torch.cuda.synchronize()
     return V, Y

@@ -44,8 +44,9 @@ def test_status_strings():
 P1, P2, P3, P4, P5, P6 = (0x100000 * (i + 1) for i in range(6))
 
 
-def shrink(V=P1, X=P2, A=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, r=16, dt=1):
-    return sg.lib.sgmv_shrink(V, X, A, P, ss, sa, N, M, d_in, r, dt, None)
+def shrink(V=P1, X=P2, A=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, r=16, dt=1, ws=0x800000,
+           wsb=1 << 20):
+    return sg.lib.sgmv_shrink(V, X, A, P, ss, sa, N, M, d_in, r, dt, ws, wsb, None)
 
 
 def expand(Y=P1, V=P2, B=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_out=64, r=16, alpha=32.0, dt=1):
@@ -87,9 +88,22 @@ def test_fused_workspace_checks():
     assert sg.lib.sgmv_workspace_bytes(2, 4, 64, 64, 12, 1) == 0
 
 
+def test_shrink_workspace_checks():
+    # a bf16 batch with few rows splits d_in between workgroups: workspace needed
+    need = sg.lib.sgmv_workspace_bytes(1, 64, 4096, 4096, 16, 1)
+    assert need > 4 * 64 * 16
+    assert shrink(M=64, d_in=4096, ws=None, wsb=0) == -6
+    # 4 tiles of 16 rows, d_in split 2 ways: 4 x 2 x 16 x 16 fp32 of partials alone
+    assert shrink(M=64, d_in=4096, wsb=4 * 2 * 16 * 16 * 4 - 1) == -6
+    assert shrink(M=64, d_in=4096, ws=0x800000 + 16, wsb=need) == -6
+    # fp32 never needs one (no MFMA path): NULL is fine; argument errors still win
+    assert shrink(M=64, d_in=4096, dt=0, ws=None, wsb=0, r=12) == -3
+
+
 def test_workspace_bytes_grows_with_rows():
-    a = sg.lib.sgmv_workspace_bytes(64, 64, 4096, 4096, 16, 1)
-    b = sg.lib.sgmv_workspace_bytes(64, 640, 4096, 4096, 16, 1)
+    # fp32 has no MFMA split, so only the fused kernel's V (M x r fp32) grows
+    a = sg.lib.sgmv_workspace_bytes(64, 64, 4096, 4096, 16, 0)
+    b = sg.lib.sgmv_workspace_bytes(64, 640, 4096, 4096, 16, 0)
     assert b - a >= 576 * 16 * 4
 
 

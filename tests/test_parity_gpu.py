@@ -256,7 +256,11 @@ def test_fused_workspace_reuse_and_reset(dev, oracle):
     sizes (fewer segments and more rows, then more segments and fewer rows,
     both dtypes) share one workspace."""
     rng = np.random.Generator(np.random.PCG64(63))
+    long_case = wl.Workload("long", 150, 1024, 264, 16, 32.0, torch.bfloat16, 3,
+                            wl.segments_from_lengths([40, 3, 107]), np.array([2, 0, 1], np.int32))
+    wl.fill_tensors(long_case, rng)
     cases = [
+        long_case,
         wl.random_case(rng, dtype=torch.float32, max_M=40, max_seg=2, ranks=(8,), max_d=256),
         wl.random_case(rng, dtype=torch.bfloat16, max_M=60, max_seg=7, ranks=(16,), max_d=256),
         wl.random_case(rng, dtype=torch.bfloat16, max_M=10, max_seg=3, ranks=(64,), max_d=256),
@@ -267,9 +271,13 @@ def test_fused_workspace_reuse_and_reset(dev, oracle):
     WS = torch.zeros(need, dtype=torch.uint8, device=dev)
     for w in cases + cases[::-1]:
         c = to_device(w, dev)
-        _, Y_ref = oracle_run(oracle, w)
+        V_ref, Y_ref = oracle_run(oracle, w)
         assert_close(run_fused(c, workspace=WS), Y_ref)
-        assert int(torch.count_nonzero(WS)) == 0, "workspace not returned to zero"
+        assert int(torch.count_nonzero(WS)) == 0, "workspace not returned to zero (fused)"
+        V, Y = run_split(c, workspace=WS)
+        assert_close(V, V_ref)
+        assert_close(Y, Y_ref)
+        assert int(torch.count_nonzero(WS)) == 0, "workspace not returned to zero (shrink)"
 
 
 def test_deterministic(dev):
@@ -304,3 +312,31 @@ def test_fused_back_to_back_fresh_values(dev, oracle):
         c = to_device(w, dev)
         _, Y_ref = oracle_run(oracle, w)
         assert np.array_equal(bits(run_fused(c, workspace=WS)), oracle_bits(oracle, Y_ref, w.dtype)), call
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_few_long_rows_split_reduction(dev, oracle, r):
+    """Batches with at most 8 tiles of long rows split d_in between
+    workgroups and combine the parts in the workspace: check the values, that
+    integer inputs stay bit-exact, and that the workspace is left zero."""
+    rng = np.random.Generator(np.random.PCG64(66 + r))
+    WS = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    for lengths in ([16], [37], [1, 20, 3, 40], [64, 64]):
+        w = wl.Workload("few_long", int(sum(lengths)), 4096, 1032, r, 2.0 * r, torch.bfloat16, 5,
+                        wl.segments_from_lengths(lengths),
+                        rng.integers(0, 5, size=len(lengths)).astype(np.int32))
+        wl.fill_tensors(w, rng)
+        c = to_device(w, dev)
+        V_ref, Y_ref = oracle_run(oracle, w)
+        V, Y = run_split(c, workspace=WS)
+        assert_close(V, V_ref, what=f"{lengths} V")
+        assert_close(Y, Y_ref, what=f"{lengths} Y")
+        assert_close(run_fused(c, workspace=WS), Y_ref, what=f"{lengths} fused")
+        assert int(torch.count_nonzero(WS)) == 0
+        wi = wl.integer_case(rng, w)
+        ci = to_device(wi, dev)
+        Vi_ref, Yi_ref = oracle_run(oracle, wi)
+        Vi, Yi = run_split(ci, workspace=WS)
+        assert np.array_equal(Vi.cpu().numpy().astype(np.float64), Vi_ref)
+        assert np.array_equal(bits(Yi), oracle_bits(oracle, Yi_ref, wi.dtype))
+        assert np.array_equal(bits(run_fused(ci, workspace=WS)), oracle_bits(oracle, Yi_ref, wi.dtype))

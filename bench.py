@@ -30,6 +30,38 @@ METRIC = "SGMV shrink+expand µs/call and HBM GB/s (% peak), 4096-d r=16, 64 ada
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 
 
+def sources_sha256():
+    """sha256 over the kernel sources, in name order (name, then bytes)."""
+    import hashlib
+    from pathlib import Path
+    h = hashlib.sha256()
+    for f in sorted((Path(ROOT) / "segmented_gather_gemm_sgmv_amd" / "csrc").glob("*")):
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, path, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary for this workload and path (FETCH_SIZE + WRITE_SIZE, each scaled
+    by what it reads for a plain 256 MiB device copy), or None when there is
+    no summary or the kernel sources have changed since it was taken."""
+    import re
+    from pathlib import Path
+    name = ("fused" if path == "fused" else "shrink_expand") + f"_{workload}.md"
+    f = Path(ROOT) / "profiles" / name
+    if not f.exists():
+        return None
+    m = re.search(r"<!-- bench-traffic (\{.*\}) -->", f.read_text())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != sources_sha256():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes"]
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -301,7 +333,8 @@ def main():
         "kernels_us": kus,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
+                     "traffic": profiled_traffic(args.workload, args.path, dom),
+                     "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)

@@ -94,6 +94,56 @@ __device__ __forceinline__ uint4 narrow<bf16_t>(const float (&in)[8]) {
                       pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
 }
 
+// Adapter address lookup for one wave. The address of a segment's adapter
+// sits behind two dependent loads (its id, then the pointer table), each a
+// full memory round trip before the weights can be requested. When the pool
+// holds at most kSpecTable adapters, every lane loads four table entries
+// right away, at the same time as the segment metadata, and the uniform id
+// then picks its entry out of registers (kSpec = true); larger pools load the
+// entry once the id is known (kSpec = false). Callers choose between the two
+// with a uniform branch around the whole work item, so that neither copy has
+// a load whose register is merged with the other's: the compiler would wait
+// for every load in flight where the two sides meet.
+constexpr int kSpecTable = 4 * kWave;
+
+template <bool kSpec>
+struct AdapterTable;
+
+template <>
+struct AdapterTable<true> {
+    uint64_t e[4];
+
+    // num_adapters >= 1: every index is clamped into the table.
+    __device__ __forceinline__ void load(const uint64_t *ptrs, int num_adapters, int lane) {
+        // Keep the loads here. Left alone, the compiler sinks them below the
+        // caller's checks on the metadata, i.e. until after it has arrived:
+        // the table is read-only, so its loads may move past anything.
+        // Hiding where the pointer came from makes them ordinary loads, which
+        // the empty barrier then holds in place.
+        asm volatile("" : "+s"(ptrs));
+        typedef __attribute__((address_space(1))) const uint64_t gconst_u64_t;
+        gconst_u64_t *g = (gconst_u64_t *)ptrs;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) e[q] = g[min(lane + q * kWave, num_adapters - 1)];
+        asm volatile("" ::: "memory");
+    }
+
+    // Address of adapter k (0 <= k < num_adapters <= kSpecTable; k uniform).
+    __device__ __forceinline__ uint64_t address(const uint64_t *, int k) const {
+        const int q = k / kWave;
+        const uint64_t v = q == 0 ? e[0] : (q == 1 ? e[1] : (q == 2 ? e[2] : e[3]));
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, k % kWave);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), k % kWave);
+        return ((uint64_t)hi << 32) | lo;
+    }
+};
+
+template <>
+struct AdapterTable<false> {
+    __device__ __forceinline__ void load(const uint64_t *, int, int) {}
+    __device__ __forceinline__ uint64_t address(const uint64_t *ptrs, int k) const { return ptrs[k]; }
+};
+
 // Segment bounds clamped into [0, M]; an inverted pair is an empty segment.
 __device__ __forceinline__ void segment_rows(const int32_t *seg_start, int s, int M, int &lo,
                                              int &hi) {

@@ -23,14 +23,18 @@
 //    rows is uniform across the workgroup and comes in through scalar loads; Y
 //    is read, updated in fp32 and rounded once on store.
 //  * fused: one launch; workgroups with the lowest ids do the shrink work,
-//    the rest the expand work. An expand workgroup waits for its segment's
-//    shrink workgroups, which have lower ids and so were dispatched first and
-//    never wait themselves. V passes between
-//    them through device-coherent (agent scope) stores and loads, published by
-//    a release increment of a per-segment arrival counter and picked up after
-//    an acquire; a second per-segment counter (departures) lets the segment's
-//    last expand workgroup return its counters and V rows to zero, so every
-//    launch leaves the whole workspace zero.
+//    the rest the expand work. An expand workgroup requests its B and Y, then
+//    waits for its segment's shrink workgroups, which have lower ids and so
+//    were dispatched first and never wait themselves. V passes between them
+//    only through device-scope (agent) atomic stores and loads, which are
+//    performed at the device's point of coherence: a producer waits until its
+//    V stores have completed, then increments a per-segment arrival counter;
+//    a consumer reads V after it has seen the full count. As every byte that
+//    crosses workgroups is accessed atomically, no cache writeback or
+//    invalidation is needed, only that completion order. A second
+//    per-segment counter (departures) lets the segment's last expand
+//    workgroup return its counters and V rows to zero, so every launch leaves
+//    the whole workspace zero.
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
@@ -73,8 +77,8 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // the block repeat the last row and are simply not stored. Straight-line
 // loads let the compiler keep all of them in flight at once.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int ROWS, bool kCoherent>
-__device__ __forceinline__ void shrink_wave(float *V, const T *X, const T *Arow, int d_in,
+template <typename T, int R, int ROWS, bool kCoherent, typename ArowFn>
+__device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
                                             int row0, int nrows, int j, int lane) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int U = ROWS <= 2 ? kShrinkUnroll : (ROWS <= 4 ? kShrinkUnroll / 2 : kShrinkUnroll / 4);
@@ -97,12 +101,15 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, const T *Arow,
             const int v = base + u * kWave + lane;
             ok[u] = v < nvec;
             vc[u] = ok[u] ? v : nvec - 1;
-            a[u] = ld16_stream(Arow + (size_t)vc[u] * VEC);
         }
+        // X first: its address is known before the adapter's
 #pragma unroll
         for (int m = 0; m < ROWS; ++m)
 #pragma unroll
             for (int u = 0; u < U; ++u) x[m][u] = ld16(xrow[m] + (size_t)vc[u] * VEC);
+        const T *Arow = arow_fn();
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = ld16_stream(Arow + (size_t)vc[u] * VEC);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (!ok[u]) a[u] = make_uint4(0, 0, 0, 0);
@@ -125,20 +132,21 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, const T *Arow,
     }
 }
 
-// All rows of one segment, rank row j, one wave.
-template <typename T, int R, bool kCoherent>
-__device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, const T *Arow, int d_in,
+// All rows of one segment, rank row j, one wave. `arow_fn()` returns the
+// address of row j of the segment's A_k.
+template <typename T, int R, bool kCoherent, typename ArowFn>
+__device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
                                                     int lo, int hi, int j, int lane) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            shrink_wave<T, R, 1, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 1, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else if (nrows <= 2)
-            shrink_wave<T, R, 2, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 2, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else if (nrows <= 4)
-            shrink_wave<T, R, 4, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 4, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else
-            shrink_wave<T, R, 8, kCoherent>(V, X, Arow, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 8, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
     }
 }
 
@@ -147,15 +155,44 @@ __device__ __forceinline__ bool takes_mfma(int rows) {
     return Elem<T>::kIsBf16 && rows >= kLongRows;
 }
 
+// Whether the vector path owns a segment: rows present, a valid adapter, and
+// too short for the MFMA path. Evaluated without short-circuits, so that the
+// compiler requests the adapter id together with the row bounds instead of
+// after them.
+template <typename T>
+__device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_adapters) {
+    return (lo < hi) & (k >= 0) & (k < num_adapters) & !takes_mfma<T>(hi - lo);
+}
+
+// One vector-path shrink item: rank row j of segment s, one wave. Returns
+// false if the segment is empty, names no valid adapter or belongs to the
+// MFMA path (then nothing is written).
+template <typename T, int R, bool kCoherent, bool kSpec>
+__device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
+                                                   int num_adapters, const int32_t *seg_start,
+                                                   const int32_t *seg_adapter, int s, int j, int M,
+                                                   int d_in, int lane) {
+    AdapterTable<kSpec> tab;
+    tab.load(A_ptrs, num_adapters, lane);
+    int lo, hi;
+    const int k = seg_adapter[s];
+    segment_rows(seg_start, s, M, lo, hi);
+    if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
+    auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
+    shrink_segment_wave<T, R, kCoherent>(V, X, arow, d_in, lo, hi, j, lane);
+    return true;
+}
+
 // Count this workgroup in; returns 1 to every thread if it was the last of
-// `expected`. Acquire-release at device scope: the last one sees every
-// earlier workgroup's stores.
+// `expected`. Every wave first waits until its own stores have completed, so
+// the last one to arrive can read every earlier workgroup's results, as long
+// as those were stored, and are read, with device-scope atomics.
 __device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected, int *s_flag) {
     wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = prev == expected - 1;
     }
     __syncthreads();
@@ -233,16 +270,17 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
     uint32_t *counters, float *partials) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = num_segments * groups;
+    if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if ((int)blockIdx.x < gemv_items) {
         const int s = blockIdx.x / groups;
         const int j = (blockIdx.x % groups) * kWavesPerBlock + (int)threadIdx.x / kWave;
         const int lane = threadIdx.x & (kWave - 1);
-        int lo, hi;
-        segment_rows(seg_start, s, M, lo, hi);
-        const int k = seg_adapter[s];
-        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
-        const T *Arow = reinterpret_cast<const T *>(A_ptrs[k]) + (size_t)j * d_in;
-        shrink_segment_wave<T, R, false>(V, X, Arow, d_in, lo, hi, j, lane);
+        if (num_adapters <= kSpecTable)
+            shrink_vector_item<T, R, false, true>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
+                                                  s, j, M, d_in, lane);
+        else
+            shrink_vector_item<T, R, false, false>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
+                                                   s, j, M, d_in, lane);
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -265,9 +303,9 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
 // ----------------------------------------------------------------------------
 // Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int RB, bool kCoherent>
-__device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, int d_out, int row0,
-                                            int nrows, int n0, bool active, float scale) {
+template <typename T, int R, int RB, bool kCoherent, typename BkFn, typename Ready>
+__device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
+                                            int nrows, int n0, bool active, float scale, Ready ready) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     // Loads are unconditional (see shrink_wave): an inactive lane reads
@@ -284,11 +322,13 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, i
         for (int e = 0; e < VEC; ++e) acc[m][e] = 0.f;
     }
 
+    const T *Bk = bk_fn();  // after the Y loads: their address is known first
 #pragma unroll 1
     for (int jc = 0; jc < R; jc += JC) {
         uint4 b[JC];
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) b[jj] = ld16_stream(Bk + (size_t)(jc + jj) * d_out + nc);
+        if (!ready()) return;  // uniform: V may be read from here on
 #pragma unroll
         for (int m = 0; m < RB; ++m) {
             float v[JC];
@@ -329,20 +369,46 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, const T *Bk, i
     }
 }
 
-template <typename T, int R, bool kCoherent>
-__device__ __forceinline__ void expand_segment(T *Y, const float *V, const T *Bk, int d_out, int lo,
-                                               int hi, int n0, bool active, float scale) {
-    for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
-        const int nrows = min(kRowBlock, hi - row0);
+// `bk_fn()` returns the address of the segment's B_k. `ready()` is called
+// (uniformly, possibly more than once) after B and Y have been requested and
+// before V is read; the rows are left untouched if it returns false. Rows
+// are taken kMaxRB (4 or 8) at a time: 8 reads B_k half as often, 4 needs
+// about 80 fewer registers per lane.
+template <typename T, int R, bool kCoherent, int kMaxRB, typename BkFn, typename Ready>
+__device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn, int d_out, int lo,
+                                               int hi, int n0, bool active, float scale, Ready ready) {
+    static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
+    for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
+        const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 1, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
-        else if (nrows <= 4)
-            expand_rows<T, R, 4, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 2, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+        else if (kMaxRB == 4 || nrows <= 4)
+            expand_rows<T, R, 4, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
         else
-            expand_rows<T, R, 8, kCoherent>(Y, V, Bk, d_out, row0, nrows, n0, active, scale);
+            expand_rows<T, R, 8, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
     }
+}
+
+// One vector-path expand item: columns n0 .. n0 + VEC - 1 (per thread) of
+// segment s; `ready` as for expand_segment. Returns false if the segment is
+// empty, names no valid adapter or belongs to the MFMA path. lo, hi receive
+// the segment's rows.
+template <typename T, int R, bool kCoherent, int kMaxRB, bool kSpec, typename ReadyFn>
+__device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
+                                                   int num_adapters, const int32_t *seg_start,
+                                                   const int32_t *seg_adapter, int s, int n0, int M,
+                                                   int d_out, float scale, int &lo, int &hi,
+                                                   ReadyFn ready) {
+    AdapterTable<kSpec> tab;
+    tab.load(B_ptrs, num_adapters, threadIdx.x & (kWave - 1));
+    const int k = seg_adapter[s];
+    segment_rows(seg_start, s, M, lo, hi);
+    if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
+    auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
+    expand_segment<T, R, kCoherent, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready);
+    return true;
 }
 
 // Items [0, N * ntiles_g): vector path, one per (segment, tile of
@@ -357,16 +423,19 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
     int ntiles_m, float scale) {
     constexpr int VEC = Elem<T>::kPerVec;
     const int gemv_items = num_segments * ntiles_g;
+    if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if ((int)blockIdx.x < gemv_items) {
         const int s = blockIdx.x / ntiles_g;
         const int tile = blockIdx.x % ntiles_g;
-        int lo, hi;
-        segment_rows(seg_start, s, M, lo, hi);
-        const int k = seg_adapter[s];
-        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
-        const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
         const int n0 = (tile * kBlock + (int)threadIdx.x) * VEC;
-        expand_segment<T, R, false>(Y, V, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
+        int lo, hi;
+        auto ready = []() { return true; };
+        if (num_adapters <= kSpecTable)
+            expand_vector_item<T, R, false, 8, true>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, s,
+                                                  n0, M, d_out, scale, lo, hi, ready);
+        else
+            expand_vector_item<T, R, false, 8, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter,
+                                                   s, n0, M, d_out, scale, lo, hi, ready);
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -382,7 +451,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
             const Piece pc = pl.p[q];
             const bf16_t *Bk = reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]);
             expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
-                                 sm, [&](size_t idx) { return V[idx]; });
+                                 sm, [&](size_t idx) { return V[idx]; }, []() { return true; });
         }
     }
 }
@@ -392,37 +461,36 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 // than every expand item (vector, then MFMA tiles).
 // ----------------------------------------------------------------------------
 
-// Thread 0 waits (bounded) until *counter reaches `target`, then acquires at
-// device scope. Returns 1 to every thread of the workgroup on success. The
-// producers hold lower workgroup ids, were dispatched earlier and never wait,
-// so the wait ends; the bound only guards against a workspace whose counters
-// were not zero on entry.
+// Thread 0 waits (bounded) until *counter reaches `target`. Returns 1 to
+// every thread of the workgroup on success; V loads issued after it see the
+// producers' V (device-scope atomics on both sides, see the top of the file).
+// The producers hold lower workgroup ids, were dispatched earlier and never
+// wait, so the wait ends; the bound only guards against a workspace whose
+// counters were not zero on entry.
 __device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag) {
     if (threadIdx.x == 0) {
         uint32_t spins = 0;
         int ok = 1;
         while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(4);  // about 256 clocks between polls
             if (++spins > (1u << 26)) {
                 ok = 0;
                 break;
             }
         }
-        // no cache of this CU or XCD may serve V older than the count seen
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         *s_flag = ok;
     }
     __syncthreads();
     return *s_flag;
 }
 
-// Publish this workgroup's V stores: every wave waits for its stores, then
-// thread 0 increments the counter with release semantics at device scope.
+// Publish this workgroup's V: every wave waits until its V stores (device-
+// scope atomics) have completed, then thread 0 increments the counter.
 __device__ __forceinline__ void publish(uint32_t *counter) {
     wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Count this workgroup out; returns 1 to every thread if it was the last of
@@ -449,14 +517,26 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
     }
 }
 
+// Row blocks of 4 in the fused kernel's vector expand keep its register
+// count low enough for two workgroups per CU (r <= 32), so that expand
+// workgroups are resident, with their B and Y requested, while the shrink
+// workgroups still run.
+constexpr int kFusedRB = 4;
+
 template <typename T, int R>
 __global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_subtiles,
-    int ks, float scale, uint32_t *seg_arrive, uint32_t *seg_depart, uint32_t *tile_arrive,
-    uint32_t *tile_depart, uint32_t *sub_arrive, float *Vws, float *partials) {
+    int ks, float scale, uint32_t *seg_counters, uint32_t *tile_counters, uint32_t *sub_arrive,
+    float *Vws, float *partials) {
+    // each segment and each 64-row tile owns one cache line of counters:
+    // word 0 counts arrivals (polled by the consumers), word 1 departures
+    uint32_t *const seg_arrive = seg_counters;
+    uint32_t *const seg_depart = seg_counters + 1;
+    uint32_t *const tile_arrive = tile_counters;
+    uint32_t *const tile_depart = tile_counters + 1;
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
@@ -466,34 +546,41 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const int a1 = a0 + round_up_xcds(num_subtiles * ks);  // MFMA shrink items (16 rows x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
+    if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if (item < a0) {
         const int s = item / groups;
         const int j = (item % groups) * kWavesPerBlock + tid / kWave;
-        int lo, hi;
-        segment_rows(seg_start, s, M, lo, hi);
-        const int k = seg_adapter[s];
-        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
-        const T *Arow = reinterpret_cast<const T *>(A_ptrs[k]) + (size_t)j * d_in;
-        shrink_segment_wave<T, R, true>(Vws, X, Arow, d_in, lo, hi, j, tid & (kWave - 1));
-        publish(&seg_arrive[s]);
+        const bool done =
+            num_adapters <= kSpecTable
+                ? shrink_vector_item<T, R, true, true>(Vws, X, A_ptrs, num_adapters, seg_start,
+                                                       seg_adapter, s, j, M, d_in, tid & (kWave - 1))
+                : shrink_vector_item<T, R, true, false>(Vws, X, A_ptrs, num_adapters, seg_start,
+                                                        seg_adapter, s, j, M, d_in, tid & (kWave - 1));
+        if (done) publish(&seg_arrive[s * kCounterStride]);
         return;
     }
     if (item >= a1 && item < a2) {
         const int e = item - a1;
         const int s = e / ntiles_g;
         const int tile = e % ntiles_g;
-        int lo, hi;
-        segment_rows(seg_start, s, M, lo, hi);
-        const int k = seg_adapter[s];
-        if (lo >= hi || k < 0 || k >= num_adapters || takes_mfma<T>(hi - lo)) return;
-        const T *Bk = reinterpret_cast<const T *>(B_ptrs[k]);
         const int n0 = (tile * kBlock + tid) * VEC;
-        if (wait_for(&seg_arrive[s], (uint32_t)groups, &s_flag))
-            expand_segment<T, R, true>(Y, Vws, Bk, d_out, lo, hi, n0, n0 < d_out, scale);
-        if (depart_last(&seg_depart[s], (uint32_t)ntiles_g, &s_flag)) {
+        int lo, hi;
+        int state = -1;  // uniform: -1 not yet waited, else the result of the wait
+        auto ready = [&]() {
+            if (state < 0) state = wait_for(&seg_arrive[s * kCounterStride], (uint32_t)groups, &s_flag);
+            return state != 0;
+        };
+        const bool valid =
+            num_adapters <= kSpecTable
+                ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vws, B_ptrs, num_adapters, seg_start,
+                                                       seg_adapter, s, n0, M, d_out, scale, lo, hi, ready)
+                : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vws, B_ptrs, num_adapters, seg_start,
+                                                        seg_adapter, s, n0, M, d_out, scale, lo, hi, ready);
+        if (!valid) return;
+        if (depart_last(&seg_depart[s * kCounterStride], (uint32_t)ntiles_g, &s_flag)) {
             // last one out: return the segment's V rows and counters to zero
             zero_rows(Vws, lo, hi, R);
-            reset_pair(&seg_arrive[s], &seg_depart[s]);
+            reset_pair(&seg_arrive[s * kCounterStride], &seg_depart[s * kCounterStride]);
         }
         return;
     }
@@ -517,7 +604,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             if (pl.n == 0) return;
             if (shrink_mfma_item<R, true>(Vws, Xb, A_ptrs, pl, d_in, st, it % ks, ks, sub_arrive,
                                           partials, sm.shrink, &s_flag))
-                publish(&tile_arrive[t0 / kTileRows]);
+                publish(&tile_arrive[(t0 / kTileRows) * kCounterStride]);
             return;
         }
         const int e = xcd_local_item(a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
@@ -535,17 +622,20 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             for (int q = 0; q < pl.n; ++q) hit |= pl.p[q].lo < q0 + kShrinkTileRows && pl.p[q].hi > q0;
             subtiles += hit;
         }
-        if (wait_for(&tile_arrive[t], subtiles, &s_flag)) {
-            for (int q = 0; q < pl.n; ++q) {
-                const Piece pc = pl.p[q];
-                expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y),
-                                     reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]), d_out, t0, pc.lo,
-                                     pc.hi, n0, scale, sm.expand, vload);
-            }
+        int state = -1;  // uniform: -1 not yet waited, else the result of the wait
+        auto ready = [&]() {
+            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], subtiles, &s_flag);
+            return state != 0;
+        };
+        for (int q = 0; q < pl.n; ++q) {
+            const Piece pc = pl.p[q];
+            expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y),
+                                 reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]), d_out, t0, pc.lo,
+                                 pc.hi, n0, scale, sm.expand, vload, ready);
         }
-        if (depart_last(&tile_depart[t], (uint32_t)ntiles_m, &s_flag)) {
+        if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {
             for (int q = 0; q < pl.n; ++q) zero_rows(Vws, pl.p[q].lo, pl.p[q].hi, R);
-            reset_pair(&tile_arrive[t], &tile_depart[t]);
+            reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
         }
     }
 }
@@ -605,8 +695,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.subtiles, L.ks, a.scale, seg_c,
-                       seg_c + a.num_segments, tile_c, tile_c + L.tiles,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.subtiles, L.ks, a.scale, seg_c, tile_c,
                        reinterpret_cast<uint32_t *>(ws + L.sub_counters),
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.partials));
     return hipGetLastError();

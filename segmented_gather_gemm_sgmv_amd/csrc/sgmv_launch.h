@@ -85,10 +85,12 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     return L;
 }
 
-// Fused workspace: two counters per segment (vector-path shrink workgroups
-// arrived, expand workgroups departed), two per 64-row tile, one per 16-row
-// shrink tile, then V (M x r fp32), then the split partials as above. Every
-// launch leaves it all zero.
+// Fused workspace: one 128-byte line of counters per segment (vector-path
+// shrink workgroups arrived, expand workgroups departed) and per 64-row tile,
+// so that consumers polling one segment do not contend with another's; then
+// one counter per 16-row shrink tile, V (M x r fp32) and the split partials
+// as above. Every launch leaves it all zero.
+constexpr int kCounterStride = 32;  // uint32 words per counter line
 struct FusedLayout {
     size_t seg_counters, tile_counters, sub_counters, v, partials, total;
     int tiles, subtiles, ks;
@@ -100,8 +102,8 @@ inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dt
     L.subtiles = dtype == kBF16 ? (M + kSubTileRows - 1) / kSubTileRows : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.seg_counters = 0;
-    L.tile_counters = 2 * sizeof(uint32_t) * (size_t)num_segments;
-    L.sub_counters = L.tile_counters + 2 * sizeof(uint32_t) * (size_t)L.tiles;
+    L.tile_counters = kCounterStride * sizeof(uint32_t) * (size_t)num_segments;
+    L.sub_counters = L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles;
     L.v = align256(L.sub_counters + sizeof(uint32_t) * (size_t)L.subtiles);
     L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
     L.total = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.subtiles * L.ks *

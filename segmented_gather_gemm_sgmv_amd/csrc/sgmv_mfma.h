@@ -295,9 +295,13 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int R, typename LoadV>
+// `ready()` is called by every thread once B and Y are on their way and
+// before V is read (a consumer of V produced in the same launch waits there);
+// if it returns false the piece is left untouched.
+template <int R, typename LoadV, typename Ready>
 __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0, int p0, int p1,
-                                  int n0, float scale, ExpandSmem<R> &sm, LoadV load_v_fn) {
+                                  int n0, float scale, ExpandSmem<R> &sm, LoadV load_v_fn,
+                                  Ready ready) {
     constexpr int K = ExpandSmem<R>::kK;
     constexpr int KS = K / 32;                                   // MFMA steps over the rank
     constexpr int kBt = ExpandSmem<R>::kBtStride;
@@ -341,6 +345,8 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
         for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
             sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
     }
+
+    if (!ready()) return;  // uniform
 
     // V rows of this wave as bf16 hi/lo halves (A operand).
     const int row = t0 + 16 * wave + i;

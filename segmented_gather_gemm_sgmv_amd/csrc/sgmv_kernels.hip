@@ -23,18 +23,18 @@
 //    rows is uniform across the workgroup and comes in through scalar loads; Y
 //    is read, updated in fp32 and rounded once on store.
 //  * fused: one launch; workgroups with the lowest ids do the shrink work,
-//    the rest the expand work. An expand workgroup requests its B and Y, then
-//    waits for its segment's shrink workgroups, which have lower ids and so
-//    were dispatched first and never wait themselves. V passes between them
-//    only through device-scope (agent) atomic stores and loads, which are
-//    performed at the device's point of coherence: a producer waits until its
-//    V stores have completed, then increments a per-segment arrival counter;
-//    a consumer reads V after it has seen the full count. As every byte that
-//    crosses workgroups is accessed atomically, no cache writeback or
-//    invalidation is needed, only that completion order. A second
-//    per-segment counter (departures) lets the segment's last expand
-//    workgroup return its counters and V rows to zero, so every launch leaves
-//    the whole workspace zero.
+//    the rest the expand work. An expand workgroup requests its B and Y,
+//    then waits for V from its segment's shrink workgroups, which have lower
+//    ids and so were dispatched first and never wait themselves. V crosses
+//    workgroups only through device-scope (agent) atomic stores and loads,
+//    performed at the device's point of coherence, so no cache writeback or
+//    invalidation is needed. On the vector path each V value travels with a
+//    ready flag in one 64-bit store and the consumer polls the values
+//    themselves. On the MFMA path a producer waits until its V stores have
+//    completed, then increments its tile's arrival counter, and a consumer
+//    reads V once it has seen the full count. A departure counter per
+//    segment or tile lets the last consumer return V and the counters to
+//    zero, so every launch leaves the whole workspace zero.
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
@@ -69,6 +69,40 @@ __device__ __forceinline__ float load_v(const float *p) {
 // (s_waitcnt with vmcnt = 0 and the other counters left alone).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// V handed from the vector shrink to the vector expand within one launch
+// travels as 64-bit pairs {value bits, ready flag}, each written by one
+// device-scope atomic store: a consumer polls the values themselves, so the
+// handoff costs one memory round trip after the store, with no counter and
+// no barrier. `V` then points at M x r such pairs.
+__device__ __forceinline__ void store_v_flagged(float *V, size_t idx, float v) {
+    const uint64_t w = (1ull << 32) | __float_as_uint(v);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(V) + idx, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr uint32_t kSpinLimit = 1u << 26;  // polls before a wait gives up (corrupt workspace)
+
+// Wave-wide: lane t < RB * JC fetches V[row0 + min(t / JC, nrows - 1)][jc + t % JC]
+// from flagged pairs, polling until every one carries its flag. Returns false
+// if the bound ran out (then `out` is meaningless).
+template <int RB, int JC>
+__device__ __forceinline__ bool poll_v_block(const float *V, int row0, int nrows, int R, int jc,
+                                             float &out) {
+    static_assert(RB * JC <= kWave, "one pair per lane");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = lane < RB * JC ? lane : 0;
+    const uint64_t *p = reinterpret_cast<const uint64_t *>(V) +
+                        (size_t)(row0 + min(t / JC, nrows - 1)) * R + jc + t % JC;
+    for (uint32_t spins = 0;; ++spins) {
+        const uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all((uint32_t)(w >> 32) != 0)) {
+            out = __uint_as_float((uint32_t)w);
+            return true;
+        }
+        if (spins > kSpinLimit) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Shrink: one wave, rank row j, up to ROWS rows of one segment.
 //
@@ -77,7 +111,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // the block repeat the last row and are simply not stored. Straight-line
 // loads let the compiler keep all of them in flight at once.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int ROWS, bool kCoherent, typename ArowFn>
+template <typename T, int R, int ROWS, bool kFlagged, typename ArowFn>
 __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
                                             int row0, int nrows, int j, int lane) {
     constexpr int VEC = Elem<T>::kPerVec;
@@ -91,6 +125,7 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
         xrow[m] = X + (size_t)(row0 + min(m, nrows - 1)) * d_in;
     }
 
+    const T *Arow = nullptr;
     for (int base = 0; base < nvec; base += kWave * U) {
         uint4 a[U];
         uint4 x[ROWS][U];
@@ -107,7 +142,9 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
         for (int m = 0; m < ROWS; ++m)
 #pragma unroll
             for (int u = 0; u < U; ++u) x[m][u] = ld16(xrow[m] + (size_t)vc[u] * VEC);
-        const T *Arow = arow_fn();
+        // once, in the first pass: asked for on every pass, the address would
+        // make each pass wait for the previous pass's loads
+        if (base == 0) Arow = arow_fn();
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] = ld16_stream(Arow + (size_t)vc[u] * VEC);
 #pragma unroll
@@ -128,25 +165,31 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
     constexpr int kSpread = kWave / ROWS;  // lanes holding the same row's total
     if ((lane & (kSpread - 1)) == 0) {
         const int m = lane / kSpread;
-        if (m < nrows) store_v<kCoherent>(V + (size_t)(row0 + m) * R + j, acc[0]);
+        const size_t idx = (size_t)(row0 + m) * R + j;
+        if (m < nrows) {
+            if constexpr (kFlagged)
+                store_v_flagged(V, idx, acc[0]);
+            else
+                V[idx] = acc[0];
+        }
     }
 }
 
 // All rows of one segment, rank row j, one wave. `arow_fn()` returns the
 // address of row j of the segment's A_k.
-template <typename T, int R, bool kCoherent, typename ArowFn>
+template <typename T, int R, bool kFlagged, typename ArowFn>
 __device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
                                                     int lo, int hi, int j, int lane) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            shrink_wave<T, R, 1, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 1, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else if (nrows <= 2)
-            shrink_wave<T, R, 2, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 2, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else if (nrows <= 4)
-            shrink_wave<T, R, 4, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 4, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
         else
-            shrink_wave<T, R, 8, kCoherent>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 8, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
     }
 }
 
@@ -167,7 +210,7 @@ __device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_ad
 // One vector-path shrink item: rank row j of segment s, one wave. Returns
 // false if the segment is empty, names no valid adapter or belongs to the
 // MFMA path (then nothing is written).
-template <typename T, int R, bool kCoherent, bool kSpec>
+template <typename T, int R, bool kFlagged, bool kSpec>
 __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int j, int M,
@@ -179,7 +222,7 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     segment_rows(seg_start, s, M, lo, hi);
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
-    shrink_segment_wave<T, R, kCoherent>(V, X, arow, d_in, lo, hi, j, lane);
+    shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane);
     return true;
 }
 
@@ -303,7 +346,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
 // ----------------------------------------------------------------------------
 // Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int RB, bool kCoherent, typename BkFn, typename Ready>
+template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready>
 __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
                                             int nrows, int n0, bool active, float scale, Ready ready) {
     constexpr int VEC = Elem<T>::kPerVec;
@@ -329,12 +372,17 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) b[jj] = ld16_stream(Bk + (size_t)(jc + jj) * d_out + nc);
         if (!ready()) return;  // uniform: V may be read from here on
+        float vl = 0.f;  // flagged V: this lane's value of the block
+        if constexpr (kFlagged) {
+            if (!poll_v_block<RB, JC>(V, row0, nrows, R, jc, vl)) return;  // wave-uniform
+        }
 #pragma unroll
         for (int m = 0; m < RB; ++m) {
             float v[JC];
-            if constexpr (kCoherent) {
+            if constexpr (kFlagged) {
 #pragma unroll
-                for (int jj = 0; jj < JC; ++jj) v[jj] = load_v<true>(V + (size_t)rowc[m] * R + jc + jj);
+                for (int jj = 0; jj < JC; ++jj)
+                    v[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vl), m * JC + jj));
             } else {
                 // uniform across the workgroup: 16-byte scalar loads
                 const float4 *vp = reinterpret_cast<const float4 *>(V + (size_t)rowc[m] * R + jc);
@@ -374,20 +422,20 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
 // before V is read; the rows are left untouched if it returns false. Rows
 // are taken kMaxRB (4 or 8) at a time: 8 reads B_k half as often, 4 needs
 // about 80 fewer registers per lane.
-template <typename T, int R, bool kCoherent, int kMaxRB, typename BkFn, typename Ready>
+template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready>
 __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn, int d_out, int lo,
                                                int hi, int n0, bool active, float scale, Ready ready) {
     static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
     for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
         const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
         else if (kMaxRB == 4 || nrows <= 4)
-            expand_rows<T, R, 4, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
-        else
-            expand_rows<T, R, 8, kCoherent>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+        else if constexpr (kMaxRB == 8)
+            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
     }
 }
 
@@ -395,7 +443,7 @@ __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn,
 // segment s; `ready` as for expand_segment. Returns false if the segment is
 // empty, names no valid adapter or belongs to the MFMA path. lo, hi receive
 // the segment's rows.
-template <typename T, int R, bool kCoherent, int kMaxRB, bool kSpec, typename ReadyFn>
+template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn>
 __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int n0, int M,
@@ -407,7 +455,7 @@ __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const u
     segment_rows(seg_start, s, M, lo, hi);
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
-    expand_segment<T, R, kCoherent, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready);
+    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready);
     return true;
 }
 
@@ -429,13 +477,10 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         const int tile = blockIdx.x % ntiles_g;
         const int n0 = (tile * kBlock + (int)threadIdx.x) * VEC;
         int lo, hi;
-        auto ready = []() { return true; };
-        if (num_adapters <= kSpecTable)
-            expand_vector_item<T, R, false, 8, true>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, s,
-                                                  n0, M, d_out, scale, lo, hi, ready);
-        else
-            expand_vector_item<T, R, false, 8, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter,
-                                                   s, n0, M, d_out, scale, lo, hi, ready);
+        // B_k's address is loaded once the id is known: reading the table
+        // early measured slower here, where Y is requested alongside B
+        expand_vector_item<T, R, false, 8, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, s,
+                                                  n0, M, d_out, scale, lo, hi, []() { return true; });
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -510,6 +555,12 @@ __device__ __forceinline__ void zero_rows(float *Vws, int lo, int hi, int R) {
     for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock) store_v<true>(Vws + (size_t)lo * R + i, 0.f);
 }
 
+__device__ __forceinline__ void zero_pairs(float *Vpairs, int lo, int hi, int R) {
+    uint64_t *p = reinterpret_cast<uint64_t *>(Vpairs) + (size_t)lo * R;
+    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock)
+        __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
     if (threadIdx.x == 0) {
         __hip_atomic_store(a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -530,10 +581,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_subtiles,
     int ks, float scale, uint32_t *seg_counters, uint32_t *tile_counters, uint32_t *sub_arrive,
-    float *Vws, float *partials) {
+    float *Vws, float *Vpairs, float *partials) {
     // each segment and each 64-row tile owns one cache line of counters:
-    // word 0 counts arrivals (polled by the consumers), word 1 departures
-    uint32_t *const seg_arrive = seg_counters;
+    // word 0 counts arrivals (polled by the consumers), word 1 departures;
+    // the vector path hands V over as flagged pairs (Vpairs) and only counts
+    // departures
     uint32_t *const seg_depart = seg_counters + 1;
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
@@ -550,13 +602,12 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     if (item < a0) {
         const int s = item / groups;
         const int j = (item % groups) * kWavesPerBlock + tid / kWave;
-        const bool done =
-            num_adapters <= kSpecTable
-                ? shrink_vector_item<T, R, true, true>(Vws, X, A_ptrs, num_adapters, seg_start,
-                                                       seg_adapter, s, j, M, d_in, tid & (kWave - 1))
-                : shrink_vector_item<T, R, true, false>(Vws, X, A_ptrs, num_adapters, seg_start,
-                                                        seg_adapter, s, j, M, d_in, tid & (kWave - 1));
-        if (done) publish(&seg_arrive[s * kCounterStride]);
+        if (num_adapters <= kSpecTable)
+            shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
+                                                 s, j, M, d_in, tid & (kWave - 1));
+        else
+            shrink_vector_item<T, R, true, false>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
+                                                  s, j, M, d_in, tid & (kWave - 1));
         return;
     }
     if (item >= a1 && item < a2) {
@@ -565,22 +616,24 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const int tile = e % ntiles_g;
         const int n0 = (tile * kBlock + tid) * VEC;
         int lo, hi;
-        int state = -1;  // uniform: -1 not yet waited, else the result of the wait
-        auto ready = [&]() {
-            if (state < 0) state = wait_for(&seg_arrive[s * kCounterStride], (uint32_t)groups, &s_flag);
-            return state != 0;
-        };
+        auto ready = []() { return true; };  // the V reads wait for their flags
+        // here B is requested before V is waited for, so B_k's address is on
+        // the critical path: read the table early when the pool is small
         const bool valid =
             num_adapters <= kSpecTable
-                ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vws, B_ptrs, num_adapters, seg_start,
-                                                       seg_adapter, s, n0, M, d_out, scale, lo, hi, ready)
-                : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vws, B_ptrs, num_adapters, seg_start,
-                                                        seg_adapter, s, n0, M, d_out, scale, lo, hi, ready);
+                ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
+                                                                 seg_adapter, s, n0, M, d_out, scale,
+                                                                 lo, hi, ready)
+                : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
+                                                                  seg_adapter, s, n0, M, d_out, scale,
+                                                                  lo, hi, ready);
         if (!valid) return;
         if (depart_last(&seg_depart[s * kCounterStride], (uint32_t)ntiles_g, &s_flag)) {
-            // last one out: return the segment's V rows and counters to zero
-            zero_rows(Vws, lo, hi, R);
-            reset_pair(&seg_arrive[s * kCounterStride], &seg_depart[s * kCounterStride]);
+            // last one out: return the segment's V pairs and its counter to zero
+            zero_pairs(Vpairs, lo, hi, R);
+            if (tid == 0)
+                __hip_atomic_store(&seg_depart[s * kCounterStride], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }
@@ -697,7 +750,8 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
                        a.d_in, a.d_out, ntiles_g, ntiles_m, L.subtiles, L.ks, a.scale, seg_c, tile_c,
                        reinterpret_cast<uint32_t *>(ws + L.sub_counters),
-                       reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.partials));
+                       reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
+                       reinterpret_cast<float *>(ws + L.partials));
     return hipGetLastError();
 }
 

@@ -85,14 +85,15 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     return L;
 }
 
-// Fused workspace: one 128-byte line of counters per segment (vector-path
-// shrink workgroups arrived, expand workgroups departed) and per 64-row tile,
-// so that consumers polling one segment do not contend with another's; then
-// one counter per 16-row shrink tile, V (M x r fp32) and the split partials
-// as above. Every launch leaves it all zero.
+// Fused workspace: one 128-byte line of counters per segment (expand
+// workgroups departed) and per 64-row tile (MFMA shrink tiles arrived,
+// expand workgroups departed), so that consumers polling one tile do not
+// contend with another's; then one counter per 16-row shrink tile, V of the
+// MFMA path (M x r fp32), the split partials as above, and V of the vector
+// path as M x r flagged 64-bit pairs. Every launch leaves it all zero.
 constexpr int kCounterStride = 32;  // uint32 words per counter line
 struct FusedLayout {
-    size_t seg_counters, tile_counters, sub_counters, v, partials, total;
+    size_t seg_counters, tile_counters, sub_counters, v, partials, vpairs, total;
     int tiles, subtiles, ks;
 };
 
@@ -106,9 +107,10 @@ inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dt
     L.sub_counters = L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles;
     L.v = align256(L.sub_counters + sizeof(uint32_t) * (size_t)L.subtiles);
     L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
-    L.total = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.subtiles * L.ks *
-                                                    kSubTileRows * (size_t)r
-                                              : 0));
+    L.vpairs = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.subtiles * L.ks *
+                                                     kSubTileRows * (size_t)r
+                                               : 0));
+    L.total = align256(L.vpairs + sizeof(uint64_t) * (size_t)M * (size_t)r);
     return L;
 }
 

@@ -1,5 +1,6 @@
-"""SGMV benchmark on one MI355X: shrink + expand (or fused) per call, through
-the C ABI, on seeded synthetic batches resident in HBM.
+"""SGMV benchmark on one MI355X: the fused shrink+expand kernel per call (or,
+with --path split, the shrink and expand kernels back to back), through the C
+ABI, on seeded synthetic batches resident in HBM.
 
 Default workload: decode with distinct adapters (d_in = d_out = 4096,
 r = 16, alpha = 32, 64 tokens in 64 length-1 segments, adapters drawn without
@@ -69,7 +70,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_distinct",
                    choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b"])
-    p.add_argument("--path", default="split", choices=["split", "fused"])
+    p.add_argument("--path", default="fused", choices=["split", "fused"])
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")

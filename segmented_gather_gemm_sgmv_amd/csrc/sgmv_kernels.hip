@@ -242,69 +242,92 @@ __device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected,
     return *s_flag;
 }
 
-// One MFMA shrink item: part `kp` (of `ks`) of d_in for the 16-row tile `st`.
-// With ks == 1 the result goes straight to V; otherwise each part leaves its
-// 16 x R partial tile in the workspace and the last part to arrive sums the
-// parts in order 0 .. ks-1, writes V, and returns the partials and the
-// counter to zero. Returns 1 (to all threads) if V of this tile was written
-// by this workgroup, i.e. the tile is complete.
+// One MFMA shrink item: part `kp` (of `ks`) of d_in for the 64-row tile `t`.
+// With ks == 1 the result goes straight to V. Otherwise each part leaves its
+// 64 x R partial tile in the workspace, in the MFMA D layout (fragment f =
+// (wave * NB + b) * 64 + lane holds four values, 16 bytes), counts itself in
+// at *split_counter, and the last part to arrive sums the parts fragment by
+// fragment in the order 0 .. ks-1, writes V, and returns the partials and the
+// counter to zero. Returns 1 (to all threads) if this workgroup completed V
+// of the tile.
 template <int R, bool kCoherent>
 __device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptrs,
-                                const PieceList &pl, int d_in, int st, int kp, int ks,
-                                uint32_t *counters, float *partials, ShrinkSmem<R> &sm, int *s_flag) {
-    const int t0 = st * kShrinkTileRows;
+                                const PieceList &pl, int d_in, int t, int kp, int ks,
+                                uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
+                                int *s_flag) {
+    constexpr int NB = ShrinkSmem<R>::kNB;
+    constexpr int kFrags = kWavesPerBlock * NB * kWave;  // 16-byte fragments per partial tile
+    constexpr uint32_t kTileBytes = kFrags * 16;
+    const int t0 = t * kShrinkTileRows;
     const int nmacro = (d_in + kMacroK - 1) / kMacroK;
     const int per = (nmacro + ks - 1) / ks;
     const int ms0 = min(nmacro, kp * per);
     const int ms1 = min(nmacro, ms0 + per);
-    float *part = partials + ((size_t)st * ks + kp) * kShrinkTileRows * R;
+    f32x4_t res[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) res[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < pl.n; ++q) {
         const Piece pc = pl.p[q];
-        shrink_piece_mfma<R>(X, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in, t0, pc.lo, pc.hi,
-                             ms0, ms1, sm, [&](int m, int j, float v) {
-                                 if (ks == 1)
-                                     store_v<kCoherent>(V + (size_t)m * R + j, v);
-                                 else
-                                     store_v<true>(part + (m - t0) * R + j, v);
-                             });
+        shrink_tile_mfma<R>(X, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in, t0, pc.lo, pc.hi,
+                            ms0, ms1, sm, res);
     }
-    if (ks == 1) return 1;
-    if (!arrive_last(&counters[st], (uint32_t)ks, s_flag)) return 0;
-    // Each thread owns at most R / 16 elements of the 16 x R tile; all their
-    // parts are loaded before any is summed or cleared, so the loads overlap.
-    constexpr int kPerThread = (kShrinkTileRows * R + kBlock - 1) / kBlock;
-    constexpr int kMaxParts = 16;
-    for (int q = 0; q < pl.n; ++q) {
-        const Piece pc = pl.p[q];
-        const int n = (pc.hi - pc.lo) * R;
+    auto in_pieces = [&](int m) {
+        bool in = false;
+        for (int q = 0; q < pl.n; ++q) in |= m >= pl.p[q].lo && m < pl.p[q].hi;
+        return in;
+    };
+    // fragment f: wave w = f / (NB * 64), block b, lane (i, g): rows
+    // t0 + 16 w + 4 g + v (v < 4), column 16 b + i
+    auto store_frag = [&](int f, const f32x4_t &val) {
+        const int lane = f % kWave, b = (f / kWave) % NB, w = f / (kWave * NB);
+        const int j = 16 * b + (lane & 15);
+        if (j >= R) return;
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-            const int idx = threadIdx.x + e * kBlock;
-            if (idx < n) {
-                const int m = pc.lo + idx / R;
-                const size_t off = (size_t)(m - t0) * R + idx % R;
-                float part_v[kMaxParts];
-#pragma unroll
-                for (int k = 0; k < kMaxParts; ++k)
-                    if (k < ks) part_v[k] = load_v<true>(partials + ((size_t)st * ks + k) * kShrinkTileRows * R + off);
-                float sum = 0.f;
-#pragma unroll
-                for (int k = 0; k < kMaxParts; ++k)
-                    if (k < ks) sum += part_v[k];
-#pragma unroll
-                for (int k = 0; k < kMaxParts; ++k)
-                    if (k < ks) store_v<true>(partials + ((size_t)st * ks + k) * kShrinkTileRows * R + off, 0.f);
-                store_v<kCoherent>(V + (size_t)m * R + idx % R, sum);
-            }
+        for (int v = 0; v < 4; ++v) {
+            const int m = t0 + 16 * w + 4 * (lane >> 4) + v;
+            if (in_pieces(m)) store_v<kCoherent>(V + (size_t)m * R + j, val[v]);
         }
+    };
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (ks == 1) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) store_frag((wave * NB + b) * kWave + lane, res[b]);
+        return 1;
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&counters[st], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float *tile_parts = partials + (size_t)t * ks * (kTileBytes / 4);
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(tile_parts, (uint32_t)ks * kTileBytes);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        store4_coherent(rs, (uint32_t)kp * kTileBytes + (uint32_t)((wave * NB + b) * kWave + lane) * 16, res[b]);
+    if (!arrive_last(split_counter, (uint32_t)ks, s_flag)) return 0;
+    // NB fragments per thread; all parts of one are loaded before any is
+    // summed or cleared, so the loads overlap.
+    constexpr int kMaxParts = 8;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int f = (int)threadIdx.x + b * kBlock;
+        f32x4_t pv[kMaxParts];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) pv[k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16);
+        f32x4_t sum = zero;
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) sum += pv[k];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16, zero);
+        store_frag(f, sum);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return 1;
 }
 
 // Items [0, N * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
-// one per (16-row tile, part of d_in) (bf16 only).
+// one per (64-row tile, part of d_in) (bf16 only).
 template <typename T, int R>
 __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
@@ -330,16 +353,16 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         __shared__ ShrinkSmem<R> sm;
         __shared__ PieceList pl;
         __shared__ int s_flag;
-        const int subtiles = (M + kShrinkTileRows - 1) / kShrinkTileRows;
-        const int item = xcd_local_item(gemv_items, subtiles * ks);
+        const int tiles = (M + kShrinkTileRows - 1) / kShrinkTileRows;
+        const int item = xcd_local_item(gemv_items, tiles * ks);
         if (item < 0) return;
-        const int st = item / ks;
-        const int t0 = st * kShrinkTileRows;
+        const int t = item / ks;
+        const int t0 = t * kShrinkTileRows;
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                       min(t0 + kShrinkTileRows, M));
         if (pl.n == 0) return;
-        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), A_ptrs, pl, d_in, st,
-                                   item % ks, ks, counters, partials, sm, &s_flag);
+        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), A_ptrs, pl, d_in, t,
+                                   item % ks, ks, ks > 1 ? counters + t : nullptr, partials, sm, &s_flag);
     }
 }
 
@@ -462,8 +485,9 @@ __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const u
 // Items [0, N * ntiles_g): vector path, one per (segment, tile of
 // kBlock * VEC columns; each wave takes kWave * VEC of them), skipping
 // segments the MFMA path owns. Items after that: MFMA tiles of kTileRows
-// batch rows by kExpandTileCols columns (bf16 only).
-template <typename T, int R>
+// batch rows by kExpandTileCols columns (bf16 only). kMaxRB: rows per block
+// of the vector path (see expand_segment).
+template <typename T, int R, int kMaxRB>
 __global__ __launch_bounds__(kBlock) void expand_kernel(
     T *__restrict__ Y, const float *__restrict__ V, const uint64_t *__restrict__ B_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
@@ -479,8 +503,8 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         int lo, hi;
         // B_k's address is loaded once the id is known: reading the table
         // early measured slower here, where Y is requested alongside B
-        expand_vector_item<T, R, false, 8, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, s,
-                                                  n0, M, d_out, scale, lo, hi, []() { return true; });
+        expand_vector_item<T, R, false, kMaxRB, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter,
+                                                       s, n0, M, d_out, scale, lo, hi, []() { return true; });
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -579,23 +603,25 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
-    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_subtiles,
-    int ks, float scale, uint32_t *seg_counters, uint32_t *tile_counters, uint32_t *sub_arrive,
-    float *Vws, float *Vpairs, float *partials) {
-    // each segment and each 64-row tile owns one cache line of counters:
-    // word 0 counts arrivals (polled by the consumers), word 1 departures;
-    // the vector path hands V over as flagged pairs (Vpairs) and only counts
-    // departures
+    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
+    int ks, float scale, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws, float *Vpairs,
+    float *partials) {
+    // each segment and each 64-row tile owns one cache line of counters. A
+    // segment's word 1 counts expand departures (the vector path hands V over
+    // as flagged pairs, Vpairs). A tile's word 0 says whether its V is
+    // complete (polled by the expand workgroups), word 1 counts departures,
+    // word 2 counts the parts of a split shrink.
     uint32_t *const seg_depart = seg_counters + 1;
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
+    uint32_t *const tile_split = tile_counters + 2;
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
     const int item = blockIdx.x;
     const int a0 = num_segments * groups;           // vector shrink items
-    const int a1 = a0 + round_up_xcds(num_subtiles * ks);  // MFMA shrink items (16 rows x part)
+    const int a1 = a0 + round_up_xcds(num_tiles * ks);    // MFMA shrink items (64 rows x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -646,18 +672,18 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
         auto vload = [&](size_t idx) { return load_v<true>(Vws + idx); };
         if (item >= a0 && item < a1) {
-            // (16-row tile, part of d_in); the workgroup that completes the
-            // tile reports to the arrival counter of its 64-row tile
-            const int it = xcd_local_item(a0, num_subtiles * ks);
+            // (64-row tile, part of d_in); the workgroup that completes the
+            // tile's V reports it on the tile's arrival word
+            const int it = xcd_local_item(a0, num_tiles * ks);
             if (it < 0) return;
-            const int st = it / ks;
-            const int t0 = st * kShrinkTileRows;
+            const int t = it / ks;
+            const int t0 = t * kShrinkTileRows;
             gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                           min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
-            if (shrink_mfma_item<R, true>(Vws, Xb, A_ptrs, pl, d_in, st, it % ks, ks, sub_arrive,
-                                          partials, sm.shrink, &s_flag))
-                publish(&tile_arrive[(t0 / kTileRows) * kCounterStride]);
+            if (shrink_mfma_item<R, true>(Vws, Xb, A_ptrs, pl, d_in, t, it % ks, ks,
+                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag))
+                publish(&tile_arrive[t * kCounterStride]);
             return;
         }
         const int e = xcd_local_item(a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
@@ -668,16 +694,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const int n0 = (e % ntiles_m) * kExpandTileCols;
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
         if (pl.n == 0) return;
-        // one arrival per 16-row sub-tile that meets a long piece
-        uint32_t subtiles = 0;
-        for (int q0 = t0; q0 < t1; q0 += kShrinkTileRows) {
-            bool hit = false;
-            for (int q = 0; q < pl.n; ++q) hit |= pl.p[q].lo < q0 + kShrinkTileRows && pl.p[q].hi > q0;
-            subtiles += hit;
-        }
+        // the shrink tile with the same rows reports once when its V is done
         int state = -1;  // uniform: -1 not yet waited, else the result of the wait
         auto ready = [&]() {
-            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], subtiles, &s_flag);
+            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], 1u, &s_flag);
             return state != 0;
         };
         for (int q = 0; q < pl.n; ++q) {
@@ -696,7 +716,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
-static_assert(kTileRows64 == kTileRows && kSubTileRows == kShrinkTileRows && kMacroSteps == kMacroK,
+static_assert(kTileRows64 == kTileRows && kTileRows64 == kShrinkTileRows && kMacroSteps == kMacroK,
               "workspace layouts must match the MFMA tiles");
 
 static int mfma_tiles(int dtype, int M) { return dtype == kBF16 ? (M + kTileRows - 1) / kTileRows : 0; }
@@ -712,7 +732,7 @@ template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const unsigned grid =
-        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.subtiles * L.ks);
+        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.tiles * L.ks);
     char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
@@ -728,9 +748,18 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
     const int tiles = mfma_tiles(a.dtype, a.M);
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
-    hipLaunchKernelGGL((expand_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
-                       reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
+    // Batches of short segments (under 16 rows on average) run mostly on the
+    // vector path: rows 8 at a time read B_k half as often. Batches of long
+    // segments run mostly on the MFMA path, whose occupancy the vector path's
+    // registers would otherwise limit: rows 4 at a time.
+    if ((int64_t)a.M < 16 * (int64_t)a.num_segments)
+        hipLaunchKernelGGL((expand_kernel<T, R, 8>), dim3(grid), dim3(kBlock), 0, st,
+                           reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
+                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
+    else
+        hipLaunchKernelGGL((expand_kernel<T, R, 4>), dim3(grid), dim3(kBlock), 0, st,
+                           reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
+                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
     return hipGetLastError();
 }
 
@@ -740,7 +769,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     const unsigned grid = (unsigned)a.num_segments * (R / kWavesPerBlock) +
-                          (unsigned)round_up_xcds(L.subtiles * L.ks) +
+                          (unsigned)round_up_xcds(L.tiles * L.ks) +
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(L.tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
@@ -748,8 +777,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.subtiles, L.ks, a.scale, seg_c, tile_c,
-                       reinterpret_cast<uint32_t *>(ws + L.sub_counters),
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.tiles, L.ks, a.scale, seg_c, tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
                        reinterpret_cast<float *>(ws + L.partials));
     return hipGetLastError();

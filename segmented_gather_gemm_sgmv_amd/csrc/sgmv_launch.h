@@ -47,68 +47,70 @@ struct FusedArgs {
     void *workspace;
 };
 
-constexpr int kSubTileRows = 16;   // rows of an MFMA shrink tile
-constexpr int kTileRows64 = 64;    // rows of an MFMA expand tile (and of a fused handoff)
+constexpr int kTileRows64 = 64;    // rows of an MFMA shrink or expand tile (and of a fused handoff)
 constexpr int kMacroSteps = 128;   // d_in elements per MFMA shrink macro step
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// How many workgroups split d_in for each 16-row MFMA shrink tile. One
-// workgroup streams only about 100 GB/s, so a batch with very few long rows
-// (at most 8 tiles of 16) spreads each tile over up to 4 workgroups, each
-// keeping at least four 128-wide macro steps per wave; larger batches
-// already have enough tiles to fill the chip and are not split.
+// How many workgroups split d_in for each 64-row MFMA shrink tile: enough for
+// about two workgroups per CU over the batch's tiles, at most 8 parts and at
+// least four 128-wide macro steps per part. One workgroup streams only a few
+// tens of GB/s, so long segments need the whole chip; the cost is a 64 x r
+// fp32 partial tile per part, summed by the last part to arrive.
 inline int shrink_ksplit(int M, int d_in) {
-    const int subtiles = (M + kSubTileRows - 1) / kSubTileRows;
+    const int tiles = (M + kTileRows64 - 1) / kTileRows64;
     const int nmacro = (d_in + kMacroSteps - 1) / kMacroSteps;
-    if (subtiles > 8) return 1;
-    return std::max(1, std::min(4, nmacro / 16));
+    if (tiles == 0) return 1;
+    int ks = (512 + tiles - 1) / tiles;
+    ks = std::min(ks, 8);
+    ks = std::min(ks, nmacro / 4);
+    return std::max(ks, 1);
 }
 
 // Shrink workspace (bf16 only, when the split is more than one part): one
-// arrival counter per 16-row tile, then the tiles' partial results
-// (tile x part x 16 x r fp32). Every launch leaves it all zero.
+// arrival counter per 64-row tile, then the tiles' partial results (tile x
+// part x 64 x max(r, 16) fp32: the MFMA tile is at least 16 columns wide).
+// Every launch leaves it all zero.
 struct ShrinkLayout {
     size_t counters, partials, total;
-    int subtiles, ks;
+    int tiles, ks;
 };
 
 inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     ShrinkLayout L;
-    L.subtiles = dtype == kBF16 ? (M + kSubTileRows - 1) / kSubTileRows : 0;
+    L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.counters = 0;
-    L.partials = align256(sizeof(uint32_t) * (size_t)L.subtiles);
-    L.total = L.ks > 1 ? align256(L.partials + sizeof(float) * (size_t)L.subtiles * L.ks *
-                                                   kSubTileRows * (size_t)r)
+    L.partials = align256(sizeof(uint32_t) * (size_t)L.tiles);
+    L.total = L.ks > 1 ? align256(L.partials + sizeof(float) * (size_t)L.tiles * L.ks *
+                                                   kTileRows64 * (size_t)std::max(r, 16))
                        : 0;
     return L;
 }
 
 // Fused workspace: one 128-byte line of counters per segment (expand
-// workgroups departed) and per 64-row tile (MFMA shrink tiles arrived,
-// expand workgroups departed), so that consumers polling one tile do not
-// contend with another's; then one counter per 16-row shrink tile, V of the
-// MFMA path (M x r fp32), the split partials as above, and V of the vector
-// path as M x r flagged 64-bit pairs. Every launch leaves it all zero.
+// workgroups departed) and per 64-row tile (V complete, expand workgroups
+// departed, split shrink parts arrived), so that consumers polling one tile
+// do not contend with another's; then V of the MFMA path (M x r fp32), the
+// split partials as above, and V of the vector path as M x r flagged 64-bit
+// pairs. Every launch leaves it all zero.
 constexpr int kCounterStride = 32;  // uint32 words per counter line
+
 struct FusedLayout {
-    size_t seg_counters, tile_counters, sub_counters, v, partials, vpairs, total;
-    int tiles, subtiles, ks;
+    size_t seg_counters, tile_counters, v, partials, vpairs, total;
+    int tiles, ks;
 };
 
 inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dtype) {
     FusedLayout L;
     L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
-    L.subtiles = dtype == kBF16 ? (M + kSubTileRows - 1) / kSubTileRows : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.seg_counters = 0;
     L.tile_counters = kCounterStride * sizeof(uint32_t) * (size_t)num_segments;
-    L.sub_counters = L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles;
-    L.v = align256(L.sub_counters + sizeof(uint32_t) * (size_t)L.subtiles);
+    L.v = align256(L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
     L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
-    L.vpairs = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.subtiles * L.ks *
-                                                     kSubTileRows * (size_t)r
+    L.vpairs = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.tiles * L.ks *
+                                                     kTileRows64 * (size_t)std::max(r, 16)
                                                : 0));
     L.total = align256(L.vpairs + sizeof(uint64_t) * (size_t)M * (size_t)r);
     return L;

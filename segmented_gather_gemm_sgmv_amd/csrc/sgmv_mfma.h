@@ -14,10 +14,11 @@
 // consecutive elements of the reduction dimension as long as its A and B
 // operands agree on which ones.
 //
-//  * shrink piece: D = X_rows (16 x d_in) . A_k^T (d_in x r) on 16-row
-//    tiles, the reduction split over the four waves; both operands go
-//    straight from HBM into registers, two macro steps in flight per lane.
-//    fp32 accumulation.
+//  * shrink tile: D = X_rows (64 x d_in) . A_k^T (d_in x r) on 64-row
+//    tiles, one wave per 16 rows; A_k is shared by the waves through LDS,
+//    X goes straight into registers, d_in may be split over several
+//    workgroups whose partial tiles are summed in a fixed order. fp32
+//    accumulation.
 //  * expand piece: D = V_rows (16 x r) . B_k (r x 128 columns). V is fp32 and
 //    enters the A operand as two bf16 halves, hi = rne(v) and lo = rne(v - hi),
 //    so hi + lo carries 16 significant bits; both halves meet the same B
@@ -161,121 +162,181 @@ __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int
 }
 
 // ----------------------------------------------------------------------------
-// Shrink piece: V[m, 0:R] = X[m, :] . A_k for rows m in [p0, p1) of the
-// 16-row tile starting at t0. The four waves split d_in: wave w takes macro
-// steps w, w+4, ... of kMacroK elements. In a macro step lane (i, g) brings,
-// for each of four MFMA k-slices q, elements kb + 32 q + 8 g .. +7 of X row i
-// and of A_k rows 16 b + i (b < NB), so the four lanes of a row read 64
-// contiguous bytes per instruction. kDepth macro steps are in flight per
-// lane. X rows are read once (streaming loads); A_k is re-read by every tile
-// of its segment and kept in cache. The waves' partial 16 x R tiles are
-// summed in LDS in a fixed order.
+// Shrink tile: V[m, 0:R] = X[m, :] . A_k for the rows m in [p0, p1) of the
+// 64-row tile starting at t0, over macro steps [ms_begin, ms_end) of d_in
+// (kMacroK elements each). Wave w owns rows t0 + 16 w .. + 15 and all R
+// columns, so the waves share the A_k chunk of a macro step (R rows x
+// kMacroK): it is loaded once per workgroup, 16 lanes per 256-byte row chunk
+// (whole cache lines), and handed to the waves through LDS. X rows go
+// straight into registers: in slice q of a macro step, lane (i, g) brings
+// elements 32 q + 8 g .. + 7 of its row, and reads the same elements of A_k
+// rows 16 b + i from LDS. kStages macro steps are in flight per lane (a ring
+// of registers); LDS holds two A_k chunks, the one being read and the one
+// being written.
+//
+// LDS layout of an A_k chunk: row j occupies 16 slots of 16 bytes; element
+// chunk c (elements 8 c .. 8 c + 7 of the macro step) of row j sits in slot
+// c ^ (j % 16). The 16 lanes that read one chunk index from 16 different rows
+// then hit 16 different slots, i.e. different banks.
 // ----------------------------------------------------------------------------
-constexpr int kShrinkTileRows = 16;
+constexpr int kShrinkTileRows = 64;
 constexpr int kMacroK = 128;
+constexpr int kChunksPerRow = kMacroK * 2 / 16;   // 16-byte chunks per A_k row of a macro step
 
 template <int R>
 struct ShrinkSmem {
-    static constexpr int kNB = R < 16 ? 1 : R / 16;            // 16-column MFMA blocks
-    static constexpr int kCols = kNB * 16;
-    float red[kBlockThreads / kWave][16 * kCols];
+    static constexpr int kNB = R < 16 ? 1 : R / 16;                   // 16-column MFMA blocks
+    static constexpr int kALoads = R * kChunksPerRow < kBlockThreads ? 1 : R * kChunksPerRow / kBlockThreads;
+    static constexpr int kStages = R >= 64 ? 2 : (R >= 32 ? 3 : 4);   // macro steps in flight
+    uint4 a[2][R * kChunksPerRow];
 };
 
-template <int NB>
-struct ShrinkOperands {
-    uint4 x[4];
-    uint4 a[NB][4];
-    uint32_t ok;  // bit q: slice q lies inside d_in
+template <int R>
+struct ShrinkStage {
+    uint4 a[ShrinkSmem<R>::kALoads];  // this thread's A_k chunks
+    uint4 x[4];                       // this lane's X elements, slices 0..3
+    uint32_t ok;                      // bits 0..3: X slice inside d_in; bits 4..: A chunk inside d_in
 };
 
-template <int R, typename StoreV>
-__device__ void shrink_piece_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int p0, int p1,
-                                  int ms_begin, int ms_end, ShrinkSmem<R> &sm, StoreV store_v_fn) {
+// Order LDS accesses across the workgroup without waiting for outstanding
+// global loads (a full barrier would also wait for every load in flight).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// On return, res[b][v] of lane (i, g) of wave w holds the tile's result for
+// row t0 + 16 w + 4 g + v and column 16 b + i (the MFMA D layout) wherever that
+// row lies in [p0, p1); elsewhere res is left as it was.
+template <int R>
+__device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int p0, int p1,
+                                 int ms_begin, int ms_end, ShrinkSmem<R> &sm,
+                                 f32x4_t (&res)[ShrinkSmem<R>::kNB]) {
     constexpr int NB = ShrinkSmem<R>::kNB;
-    constexpr int kCols = ShrinkSmem<R>::kCols;
-    constexpr int kWaves = kBlockThreads / kWave;
-    constexpr int kDepth = NB == 1 ? 4 : (NB == 2 ? 3 : 2);      // macro steps in flight
+    constexpr int kALoads = ShrinkSmem<R>::kALoads;
+    constexpr int S = ShrinkSmem<R>::kStages;
+    constexpr int kAChunks = R * kChunksPerRow;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int g = lane >> 4;
     const int i = lane & 15;
-    const int row = t0 + i;
-    const bool row_ok = row >= p0 && row < p1;
-    const bf16_t *xrow = X + (size_t)(row_ok ? row : p0) * d_in;  // others: never stored
-    // This piece covers macro steps [ms_begin, ms_end) of d_in. Every wave
-    // runs the same number of steps, padded to a multiple of kDepth; a step
-    // past the end loads clamped addresses and zeroes its X, so loads never
-    // sit behind a branch and all kDepth steps stay in flight.
-    const int nper = (ms_end - ms_begin + kWaves - 1) / kWaves;
-    const int niter = (nper + kDepth - 1) / kDepth * kDepth;
+    const int row = t0 + 16 * wave + i;
+    const bf16_t *xrow = X + (size_t)min(max(row, p0), p1 - 1) * d_in;  // rows outside: never stored
+    // Every step of the loop is straight-line: a step past ms_end (padding to
+    // a multiple of S) or a slice past d_in loads a clamped address and its
+    // operands are zeroed, never skipped, so each group of loads stays in
+    // flight until its turn.
+    const int niter = (ms_end - ms_begin + S - 1) / S * S;
 
-    // A slice outside the piece's range loads from a clamped address; its X is
-    // replaced by zero when the MFMA operand is formed (never by writing over
-    // the load's destination, which would make the load wait).
-    auto load = [&](ShrinkOperands<NB> &op, int it) {
-        const int ms = ms_begin + wave + it * kWaves;
-        const int kb = ms * kMacroK + 8 * g;
-        op.ok = 0;
+    auto load = [&](ShrinkStage<R> &st, int it) {
+        const int ms = ms_begin + it;
+        const bool step_ok = ms < ms_end;
+        const int kb = max(0, min(ms, ms_end - 1)) * kMacroK;  // an empty range loads step 0
+        st.ok = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int k = kb + 32 * q;
-            const bool ok = ms < ms_end && k < d_in;
-            const int kc = ok ? k : d_in - 8;
-            op.ok |= (uint32_t)ok << q;
-            op.x[q] = ld16_stream(xrow + kc);
+            const int k = kb + 32 * q + 8 * g;
+            const bool ok = step_ok && k < d_in;
+            st.ok |= (uint32_t)ok << q;
+            st.x[q] = ld16_stream(xrow + (ok ? k : d_in - 8));
+        }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int j = min(16 * b + i, R - 1);  // columns past R are never stored
-                op.a[b][q] = ld16(Ak + (size_t)j * d_in + kc);
-            }
+        for (int u = 0; u < kALoads; ++u) {
+            const int id = min(u * kBlockThreads + tid, kAChunks - 1);  // R = 8: half the threads repeat
+            const int k = kb + 8 * (id % kChunksPerRow);
+            const bool ok = step_ok && k < d_in;
+            st.ok |= (uint32_t)ok << (4 + u);
+            st.a[u] = ld16(Ak + (size_t)(id / kChunksPerRow) * d_in + (ok ? k : d_in - 8));
         }
     };
+
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // The memory counter retires loads in issue order, so each group of loads
-    // must stay where it is written: scheduling barriers stop the compiler
-    // from interleaving the groups, and consuming the oldest group then waits
-    // only for that group.
-    ShrinkOperands<NB> buf[kDepth];
+    // Consume one stage: its A_k chunks go to LDS buffer `buf`, then every
+    // wave multiplies its X slices with the whole chunk.
+    auto consume = [&](const ShrinkStage<R> &st, int buf) {
 #pragma unroll
-    for (int u = 0; u < kDepth - 1; ++u) {
-        load(buf[u], u);
+        for (int u = 0; u < kALoads; ++u) {
+            const int id = u * kBlockThreads + tid;
+            if (id < kAChunks) {
+                const int j = id / kChunksPerRow;
+                const int c = id % kChunksPerRow;
+                const uint4 v = ((st.ok >> (4 + u)) & 1u) ? st.a[u] : make_uint4(0, 0, 0, 0);
+                sm.a[buf][j * kChunksPerRow + (c ^ (j & 15))] = v;
+            }
+        }
+        lds_barrier();
+        // The A operands of slice q + 1 are requested from LDS before the
+        // MFMAs of slice q are issued, so LDS latency overlaps the math
+        // instead of preceding every instruction.
+        auto lds_slice = [&](uint4 (&av)[NB], int q) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int j = min(16 * b + i, R - 1);  // columns past R are never stored
+                av[b] = sm.a[buf][j * kChunksPerRow + ((4 * q + g) ^ (j & 15))];
+            }
+        };
+        uint4 av[2][NB];
+        lds_slice(av[0], 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q + 1 < 4) lds_slice(av[(q + 1) & 1], q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 xq = ((st.ok >> q) & 1u) ? st.x[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[b] = mfma_bf16(as_bf16x8(xq), as_bf16x8(av[q & 1][b]), acc[b]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // The memory counter retires loads in issue order: scheduling barriers
+    // keep each step's group of loads together, so consuming the oldest
+    // group waits for that group only.
+    ShrinkStage<R> ring[S];
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) {
+        load(ring[u], u);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int it0 = 0; it0 < niter; it0 += kDepth) {
+    for (int it0 = 0; it0 < niter; it0 += S) {
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
-            load(buf[(u + kDepth - 1) % kDepth], it0 + u + kDepth - 1);
+        for (int u = 0; u < S; ++u) {
+            load(ring[(u + S - 1) % S], it0 + u + S - 1);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 xq = ((buf[u].ok >> q) & 1u) ? buf[u].x[q] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] = mfma_bf16(as_bf16x8(xq), as_bf16x8(buf[u].a[b][q]), acc[b]);
-            }
+            consume(ring[u], (it0 + u) & 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    lds_barrier();  // the LDS buffers are free for whatever comes next
 
-    // fixed-order sum of the four waves' partial tiles
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int v = 0; v < 4; ++v) {
+        const int m = t0 + 16 * wave + 4 * g + v;
+        const bool in_piece = m >= p0 && m < p1;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sm.red[wave][(4 * g + v) * kCols + 16 * b + i] = acc[b][v];
-    __syncthreads();
-    for (int idx = tid; idx < 16 * R; idx += kBlockThreads) {
-        const int m = idx / R;
-        const int j = idx % R;
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += sm.red[w][m * kCols + j];
-        if (t0 + m >= p0 && t0 + m < p1) store_v_fn(t0 + m, j, sum);
+        for (int b = 0; b < NB; ++b) res[b][v] = in_piece ? acc[b][v] : res[b][v];
     }
-    __syncthreads();
+}
+
+// Device-scope (agent) 16-byte loads and stores through a buffer resource:
+// the partial tiles of a split shrink are written by one workgroup and read
+// by another, possibly on another XCD, so they bypass the non-coherent
+// caches. The resource also bounds every access to [base, base + bytes).
+constexpr int kCoherentPolicy = 16;  // cache policy bits: device scope
+typedef uint32_t u32x4_t_ __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(float *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4_t load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherentPolicy));
+}
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t_, v), r, byte_off, 0, kCoherentPolicy);
 }
 
 // ----------------------------------------------------------------------------

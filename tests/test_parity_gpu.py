@@ -252,9 +252,9 @@ def test_guard_bands(dev, oracle):
 
 
 def test_fused_workspace_reuse_and_reset(dev, oracle):
-    """Every fused call leaves the whole workspace zero, so calls of any
-    sizes (fewer segments and more rows, then more segments and fewer rows,
-    both dtypes) share one workspace."""
+    """Every call leaves the whole workspace zero, so calls of any sizes
+    (fewer segments and more rows, then more segments and fewer rows, both
+    dtypes, fused and split) share one workspace."""
     rng = np.random.Generator(np.random.PCG64(63))
     long_case = wl.Workload("long", 150, 1024, 264, 16, 32.0, torch.bfloat16, 3,
                             wl.segments_from_lengths([40, 3, 107]), np.array([2, 0, 1], np.int32))
@@ -314,15 +314,18 @@ def test_fused_back_to_back_fresh_values(dev, oracle):
         assert np.array_equal(bits(run_fused(c, workspace=WS)), oracle_bits(oracle, Y_ref, w.dtype)), call
 
 
-@pytest.mark.parametrize("r", [16, 64])
-def test_few_long_rows_split_reduction(dev, oracle, r):
-    """Batches with at most 8 tiles of long rows split d_in between
-    workgroups and combine the parts in the workspace: check the values, that
-    integer inputs stay bit-exact, and that the workspace is left zero."""
-    rng = np.random.Generator(np.random.PCG64(66 + r))
-    WS = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
-    for lengths in ([16], [37], [1, 20, 3, 40], [64, 64]):
-        w = wl.Workload("few_long", int(sum(lengths)), 4096, 1032, r, 2.0 * r, torch.bfloat16, 5,
+@pytest.mark.parametrize("r,d_in", [(16, 4096), (64, 4096), (16, 4104), (32, 4224)])
+def test_few_long_rows_split_reduction(dev, oracle, r, d_in):
+    """Batches with few tiles of long rows split d_in between workgroups and
+    combine the parts in the workspace, in a fixed order: check the values
+    that integer inputs stay bit-exact and that the workspace is left zero.
+    d_in = 4104 ends in a partial
+    macro step; with 4104 and 4224 (33 macro steps in 8 parts) the last part
+    has no steps at all and contributes zeros."""
+    rng = np.random.Generator(np.random.PCG64(66 + r + d_in))
+    WS = torch.zeros(1 << 23, dtype=torch.uint8, device=dev)
+    for lengths in ([16], [37], [1, 20, 3, 40], [64, 64], [70, 2, 150]):
+        w = wl.Workload("few_long", int(sum(lengths)), d_in, 1032, r, 2.0 * r, torch.bfloat16, 5,
                         wl.segments_from_lengths(lengths),
                         rng.integers(0, 5, size=len(lengths)).astype(np.int32))
         wl.fill_tensors(w, rng)

@@ -325,7 +325,19 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptr
     return 1;
 }
 
-// Items [0, N * R / 4): vector path, one per (segment, group of 4 rank rows),
+// Vector shrink items: segment s, rank group g (of `groups`), numbered so
+// that all groups of one segment get ids of the same residue mod 8, i.e.
+// run on one XCD (workgroups are dealt to the XCDs round-robin by id) and
+// fetch the segment's X rows into one L2 instead of several. Needs
+// round_up_xcds(N) * groups items; returns false for the padding.
+__device__ __forceinline__ bool vector_shrink_item(int b, int num_segments, int groups, int &s, int &g) {
+    const int chunk = b / (kXcds * groups);
+    g = (b / kXcds) % groups;
+    s = chunk * kXcds + b % kXcds;
+    return s < num_segments;
+}
+
+// Items [0, round_up_xcds(N) * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
 // one per (64-row tile, part of d_in) (bf16 only).
 template <typename T, int R>
@@ -335,11 +347,12 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
     const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int ks,
     uint32_t *counters, float *partials) {
     constexpr int groups = R / kWavesPerBlock;
-    const int gemv_items = num_segments * groups;
+    const int gemv_items = round_up_xcds(num_segments) * groups;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if ((int)blockIdx.x < gemv_items) {
-        const int s = blockIdx.x / groups;
-        const int j = (blockIdx.x % groups) * kWavesPerBlock + (int)threadIdx.x / kWave;
+        int s, grp;
+        if (!vector_shrink_item(blockIdx.x, num_segments, groups, s, grp)) return;
+        const int j = grp * kWavesPerBlock + (int)threadIdx.x / kWave;
         const int lane = threadIdx.x & (kWave - 1);
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, false, true>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
@@ -620,14 +633,15 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     __shared__ int s_flag;
     const int tid = threadIdx.x;
     const int item = blockIdx.x;
-    const int a0 = num_segments * groups;           // vector shrink items
+    const int a0 = round_up_xcds(num_segments) * groups;  // vector shrink items
     const int a1 = a0 + round_up_xcds(num_tiles * ks);    // MFMA shrink items (64 rows x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if (item < a0) {
-        const int s = item / groups;
-        const int j = (item % groups) * kWavesPerBlock + tid / kWave;
+        int s, grp;
+        if (!vector_shrink_item(item, num_segments, groups, s, grp)) return;
+        const int j = grp * kWavesPerBlock + tid / kWave;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
                                                  s, j, M, d_in, tid & (kWave - 1));
@@ -732,7 +746,7 @@ template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const unsigned grid =
-        (unsigned)a.num_segments * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.tiles * L.ks);
+        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.tiles * L.ks);
     char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
@@ -768,7 +782,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     const FusedLayout L = fused_layout(a.num_segments, a.M, a.d_in, a.r, a.dtype);
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
-    const unsigned grid = (unsigned)a.num_segments * (R / kWavesPerBlock) +
+    const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
                           (unsigned)round_up_xcds(L.tiles * L.ks) +
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(L.tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);

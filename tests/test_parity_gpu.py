@@ -343,3 +343,26 @@ def test_few_long_rows_split_reduction(dev, oracle, r, d_in):
         assert np.array_equal(Vi.cpu().numpy().astype(np.float64), Vi_ref)
         assert np.array_equal(bits(Yi), oracle_bits(oracle, Yi_ref, wi.dtype))
         assert np.array_equal(bits(run_fused(ci, workspace=WS)), oracle_bits(oracle, Yi_ref, wi.dtype))
+
+
+@pytest.mark.parametrize("P", [255, 256, 257])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pool_table_boundaries(dev, oracle, P, dtype):
+    """Pools of up to 256 adapters are looked up from a copy of the whole
+    pointer table held in registers (four entries per lane), larger ones by a
+    dependent load: ids in every quarter of the table, and the last entry,
+    must reach the right adapter on both sides of the limit (integer inputs,
+    bitwise)."""
+    rng = np.random.Generator(np.random.PCG64(70 + P))
+    lengths = [1, 1, 3, 1, 2, 1, 1, 1, 1, 5]
+    ids = np.array([0, 63, 64, 127, 128, 191, 192, P - 1, P // 2, 255 % P], np.int32)
+    w = wl.Workload("pool", int(sum(lengths)), 256, 264, 16, 32.0, dtype, P,
+                    wl.segments_from_lengths(lengths), ids)
+    wl.fill_tensors(w, rng)
+    wl.integer_case(rng, w)
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    V, Y = run_split(c)
+    assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
+    assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, dtype))
+    assert np.array_equal(bits(run_fused(c)), oracle_bits(oracle, Y_ref, dtype))

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         for (int q = 0; q < pl.n; ++q) {
             const Piece pc = pl.p[q];
             const bf16_t *Bk = reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]);
-            expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
+            expand_piece_mfma<R, true>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
                                  sm, [&](size_t idx) { return V[idx]; }, []() { return true; });
         }
     }
@@ -716,7 +716,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         };
         for (int q = 0; q < pl.n; ++q) {
             const Piece pc = pl.p[q];
-            expand_piece_mfma<R>(reinterpret_cast<bf16_t *>(Y),
+            expand_piece_mfma<R, false>(reinterpret_cast<bf16_t *>(Y),
                                  reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]), d_out, t0, pc.lo,
                                  pc.hi, n0, scale, sm.expand, vload, ready);
         }

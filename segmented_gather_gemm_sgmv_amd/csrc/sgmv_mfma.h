@@ -348,8 +348,14 @@ struct ExpandSmem {
     static constexpr int kK = R < 32 ? 32 : R;                  // reduction length, zero-padded
     static constexpr int kBtStride = kK + 8;                     // bf16 per transposed row (padded)
     static constexpr int kYsStride = kExpandTileCols + 4;        // floats per staged output row
-    uint16_t bt[kExpandTileCols * kBtStride];                    // B tile, [n][k]
-    float ys[kTileRows * kYsStride];                             // delta tile, [m][n]
+    // The delta tile is staged over the B tile once every MFMA has read it,
+    // which leaves room for three workgroups per CU.
+    union __attribute__((aligned(16))) {
+        uint16_t bt[kExpandTileCols * kBtStride];                // B tile, [n][k]
+        uint4 bt16[kExpandTileCols * kBtStride / 8];             // the same, 16-byte vectors
+        float ys[kTileRows * kYsStride];                         // delta tile, [m][n]
+    };
+    static_assert(kBtStride % 8 == 0, "B tile rows must be whole 16-byte vectors");
 };
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -359,7 +365,9 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // `ready()` is called by every thread once B and Y are on their way and
 // before V is read (a consumer of V produced in the same launch waits there);
 // if it returns false the piece is left untouched.
-template <int R, typename LoadV, typename Ready>
+// kVEarly: V is final before the launch (a separate shrink), so it is
+// requested together with B instead of after the B tile is staged.
+template <int R, bool kVEarly, typename LoadV, typename Ready>
 __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0, int p0, int p1,
                                   int n0, float scale, ExpandSmem<R> &sm, LoadV load_v_fn,
                                   Ready ready) {
@@ -386,6 +394,45 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
         yv[q] = ld16(Y + (size_t)(ok ? m : p0) * d_out + (ok ? n : 0));  // others: never stored
     }
 
+    // V rows of this wave (A operand): lane (i, g) needs columns
+    // ks * 32 + 8 g .. + 7 of row t0 + 16 w + i. Fetched raw first, then split
+    // into bf16 hi/lo halves once the values are needed.
+    const int row = t0 + 16 * wave + i;
+    const bool row_ok = row >= p0 && row < p1;
+    float vraw[KS][8];
+    auto fetch_v = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // rows outside the piece are never stored; rank columns past R
+                // meet zero rows of the staged B tile but are zeroed anyway so
+                // a non-finite value cannot leak into a valid row
+                const int j = ks * 32 + 8 * g + e;
+                const float v = load_v_fn((size_t)(row_ok ? row : p0) * R + min(j, R - 1));
+                vraw[ks][e] = j < R ? v : 0.f;
+            }
+    };
+    bf16x8_t ahi[KS], alo[KS];
+    auto split_v = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float v0 = vraw[ks][2 * e2], v1 = vraw[ks][2 * e2 + 1];
+                const uint32_t hb0 = bf16_bits(v0), hb1 = bf16_bits(v1);
+                const float r0 = v0 - __uint_as_float(hb0 << 16);
+                const float r1 = v1 - __uint_as_float(hb1 << 16);
+                h[e2] = hb0 | (hb1 << 16);
+                l[e2] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+            }
+            ahi[ks] = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+            alo[ks] = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+        }
+    };
+    if constexpr (kVEarly) fetch_v();
+
     // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
     for (int idx = tid; idx < (R / 2) * kColVecs; idx += kBlockThreads) {
         const int jp = idx / kColVecs;
@@ -408,50 +455,34 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
     }
 
     if (!ready()) return;  // uniform
-
-    // V rows of this wave as bf16 hi/lo halves (A operand).
-    const int row = t0 + 16 * wave + i;
-    const bool row_ok = row >= p0 && row < p1;
-    bf16x8_t ahi[KS], alo[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            float v2[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                // rows outside the piece are never stored; rank columns past R
-                // meet zero rows of the staged B tile but are zeroed anyway so
-                // a non-finite value cannot leak into a valid row
-                const int j = ks * 32 + 8 * g + 2 * e2 + u;
-                const float v = load_v_fn((size_t)(row_ok ? row : p0) * R + min(j, R - 1));
-                v2[u] = j < R ? v : 0.f;
-            }
-            const uint32_t hb0 = bf16_bits(v2[0]), hb1 = bf16_bits(v2[1]);
-            const float r0 = v2[0] - __uint_as_float(hb0 << 16);
-            const float r1 = v2[1] - __uint_as_float(hb1 << 16);
-            h[e2] = hb0 | (hb1 << 16);
-            l[e2] = bf16_bits(r0) | (bf16_bits(r1) << 16);
-        }
-        ahi[ks] = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
-        alo[ks] = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
-    }
+    if constexpr (!kVEarly) fetch_v();
+    split_v();
     __syncthreads();  // B tile in LDS
 
+    // All B operands first, then eight independent accumulator chains, so
+    // neither LDS nor MFMA latency sits between consecutive instructions.
+    constexpr int NBLK = kExpandTileCols / 16;
+    uint4 bv[KS][NBLK];
 #pragma unroll
-    for (int b = 0; b < kExpandTileCols / 16; ++b) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t bv = as_bf16x8(
-                *reinterpret_cast<const uint4 *>(&sm.bt[(16 * b + i) * kBt + ks * 32 + 8 * g]));
-            acc = mfma_bf16(ahi[ks], bv, acc);
-            acc = mfma_bf16(alo[ks], bv, acc);
-        }
+        for (int b = 0; b < NBLK; ++b)
+            bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
+    f32x4_t acc[NBLK];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[v];
+    for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(ahi[ks], as_bf16x8(bv[ks][b]), acc[b]);
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(alo[ks], as_bf16x8(bv[ks][b]), acc[b]);
     }
+    __syncthreads();  // every wave is done with the B tile, whose LDS the delta tile reuses
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[b][v];
     __syncthreads();  // delta tile in LDS
 
 #pragma unroll

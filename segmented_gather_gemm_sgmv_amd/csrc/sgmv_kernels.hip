@@ -301,26 +301,33 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptr
     for (int b = 0; b < NB; ++b)
         store4_coherent(rs, (uint32_t)kp * kTileBytes + (uint32_t)((wave * NB + b) * kWave + lane) * 16, res[b]);
     if (!arrive_last(split_counter, (uint32_t)ks, s_flag)) return 0;
-    // NB fragments per thread; all parts of one are loaded before any is
-    // summed or cleared, so the loads overlap.
+    // NB fragments per thread. Every part of every fragment is requested
+    // before anything is summed or cleared: a load placed after a store to
+    // the same buffer would wait for it, which made the sum a chain of
+    // device-scope round trips.
     constexpr int kMaxParts = 8;
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t pv[NB][kMaxParts];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) pv[b][k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)((int)threadIdx.x + b * kBlock) * 16);
+    f32x4_t sum[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const int f = (int)threadIdx.x + b * kBlock;
-        f32x4_t pv[kMaxParts];
+        sum[b] = zero;
 #pragma unroll
         for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) pv[k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16);
-        f32x4_t sum = zero;
-#pragma unroll
-        for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) sum += pv[k];
-#pragma unroll
-        for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16, zero);
-        store_frag(f, sum);
+            if (k < ks) sum[b] += pv[b][k];
     }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)((int)threadIdx.x + b * kBlock) * 16, zero);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) store_frag((int)threadIdx.x + b * kBlock, sum[b]);
     if (threadIdx.x == 0) __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return 1;
 }

@@ -250,8 +250,8 @@ __device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected,
 // fragment in the order 0 .. ks-1, writes V, and returns the partials and the
 // counter to zero. Returns 1 (to all threads) if this workgroup completed V
 // of the tile.
-template <int R, bool kCoherent>
-__device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptrs,
+template <int R, bool kCoherent, typename AkOf>
+__device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
                                 uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
                                 int *s_flag) {
@@ -268,7 +268,7 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, const uint64_t *A_ptr
     for (int b = 0; b < NB; ++b) res[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < pl.n; ++q) {
         const Piece pc = pl.p[q];
-        shrink_tile_mfma<R>(X, reinterpret_cast<const bf16_t *>(A_ptrs[pc.k]), d_in, t0, pc.lo, pc.hi,
+        shrink_tile_mfma<R>(X, ak_of(pc.k), d_in, t0, pc.lo, pc.hi,
                             ms0, ms1, sm, res);
     }
     auto in_pieces = [&](int m) {
@@ -344,6 +344,23 @@ __device__ __forceinline__ bool vector_shrink_item(int b, int num_segments, int 
     return s < num_segments;
 }
 
+// Adapter addresses for an MFMA item: with at most kSpecTable adapters the
+// table is read once per wave, together with the segment metadata, instead
+// of entry by entry once the pieces are known.
+struct MfmaAdapters {
+    AdapterTable<true> tab;
+    const uint64_t *ptrs;
+    int num_adapters;
+
+    __device__ __forceinline__ MfmaAdapters(const uint64_t *p, int n) : ptrs(p), num_adapters(n) {
+        tab.load(p, n, threadIdx.x & (kWave - 1));
+    }
+    // k: a valid adapter id, uniform across the workgroup
+    __device__ __forceinline__ const bf16_t *operator()(int k) const {
+        return reinterpret_cast<const bf16_t *>(num_adapters <= kSpecTable ? tab.address(ptrs, k) : ptrs[k]);
+    }
+};
+
 // Items [0, round_up_xcds(N) * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
 // one per (64-row tile, part of d_in) (bf16 only).
@@ -378,10 +395,11 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         if (item < 0) return;
         const int t = item / ks;
         const int t0 = t * kShrinkTileRows;
+        const MfmaAdapters ak_of(A_ptrs, num_adapters);
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                       min(t0 + kShrinkTileRows, M));
         if (pl.n == 0) return;
-        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), A_ptrs, pl, d_in, t,
+        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
                                    item % ks, ks, ks > 1 ? counters + t : nullptr, partials, sm, &s_flag);
     }
 }
@@ -535,10 +553,11 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         const int t0 = (e / ntiles_m) * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
+        const MfmaAdapters bk_of(B_ptrs, num_adapters);
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
         for (int q = 0; q < pl.n; ++q) {
             const Piece pc = pl.p[q];
-            const bf16_t *Bk = reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]);
+            const bf16_t *Bk = bk_of(pc.k);
             expand_piece_mfma<R, true>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
                                  sm, [&](size_t idx) { return V[idx]; }, []() { return true; });
         }
@@ -699,10 +718,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             if (it < 0) return;
             const int t = it / ks;
             const int t0 = t * kShrinkTileRows;
+            const MfmaAdapters ak_of(A_ptrs, num_adapters);
             gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                           min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
-            if (shrink_mfma_item<R, true>(Vws, Xb, A_ptrs, pl, d_in, t, it % ks, ks,
+            if (shrink_mfma_item<R, true>(Vws, Xb, ak_of, pl, d_in, t, it % ks, ks,
                                           &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag))
                 publish(&tile_arrive[t * kCounterStride]);
             return;
@@ -713,6 +733,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const int t0 = t * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
+        const MfmaAdapters bk_of(B_ptrs, num_adapters);
         gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
         if (pl.n == 0) return;
         // the shrink tile with the same rows reports once when its V is done
@@ -724,7 +745,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         for (int q = 0; q < pl.n; ++q) {
             const Piece pc = pl.p[q];
             expand_piece_mfma<R, false>(reinterpret_cast<bf16_t *>(Y),
-                                 reinterpret_cast<const bf16_t *>(B_ptrs[pc.k]), d_out, t0, pc.lo,
+                                 bk_of(pc.k), d_out, t0, pc.lo,
                                  pc.hi, n0, scale, sm.expand, vload, ready);
         }
         if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {

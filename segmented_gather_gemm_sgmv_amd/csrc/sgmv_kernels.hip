@@ -25,14 +25,15 @@
 //  * fused: one launch; workgroups with the lowest ids do the shrink work,
 //    the rest the expand work. An expand workgroup requests its B and Y,
 //    then waits for V from its segment's shrink workgroups, which have lower
-//    ids and so were dispatched first and never wait themselves. V crosses
+//    ids and so were dispatched first and never wait for an expand
+//    workgroup. V crosses
 //    workgroups only through device-scope (agent) atomic stores and loads,
 //    performed at the device's point of coherence, so no cache writeback or
 //    invalidation is needed. On the vector path each V value travels with a
 //    ready flag in one 64-bit store and the consumer polls the values
-//    themselves. On the MFMA path a producer waits until its V stores have
-//    completed, then increments its tile's arrival counter, and a consumer
-//    reads V once it has seen the full count. A departure counter per
+//    themselves. On the MFMA path each part of a shrink tile waits until its
+//    V stores have completed, then increments the tile's arrival counter,
+//    and a consumer reads V once it has seen every part. A departure counter per
 //    segment or tile lets the last consumer return V and the counters to
 //    zero, so every launch leaves the whole workspace zero.
 
@@ -226,12 +227,42 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     return true;
 }
 
-// Count this workgroup in; returns 1 to every thread if it was the last of
-// `expected`. Every wave first waits until its own stores have completed, so
-// the last one to arrive can read every earlier workgroup's results, as long
-// as those were stored, and are read, with device-scope atomics.
-__device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected, int *s_flag) {
+// Thread 0 waits (bounded) until *counter reaches `target`. Returns 1 to
+// every thread of the workgroup on success; loads issued after it see what
+// the counted workgroups stored before counting themselves in (device-scope
+// atomics on both sides, see the top of the file). Each caller explains why
+// the workgroups it waits for are dispatched; the bound only guards against
+// a workspace whose counters were not zero on entry.
+__device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag) {
+    if (threadIdx.x == 0) {
+        uint32_t spins = 0;
+        int ok = 1;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(4);  // about 256 clocks between polls
+            if (++spins > (1u << 26)) {
+                ok = 0;
+                break;
+            }
+        }
+        *s_flag = ok;
+    }
+    __syncthreads();
+    return *s_flag;
+}
+
+// Publish this workgroup's results: every wave waits until its stores
+// (device-scope atomics) have completed, then thread 0 increments the
+// counter.
+__device__ __forceinline__ void publish(uint32_t *counter) {
     wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this workgroup out; returns 1 to every thread if it was the last of
+// `expected` (all of them have finished reading V by then).
+__device__ __forceinline__ int depart_last(uint32_t *counter, uint32_t expected, int *s_flag) {
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev =
@@ -242,14 +273,41 @@ __device__ __forceinline__ int arrive_last(uint32_t *counter, uint32_t expected,
     return *s_flag;
 }
 
+__device__ __forceinline__ void zero_rows(float *Vws, int lo, int hi, int R) {
+    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock) store_v<true>(Vws + (size_t)lo * R + i, 0.f);
+}
+
+__device__ __forceinline__ void zero_pairs(float *Vpairs, int lo, int hi, int R) {
+    uint64_t *p = reinterpret_cast<uint64_t *>(Vpairs) + (size_t)lo * R;
+    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock)
+        __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // One MFMA shrink item: part `kp` (of `ks`) of d_in for the 64-row tile `t`.
 // With ks == 1 the result goes straight to V. Otherwise each part leaves its
 // 64 x R partial tile in the workspace, in the MFMA D layout (fragment f =
 // (wave * NB + b) * 64 + lane holds four values, 16 bytes), counts itself in
-// at *split_counter, and the last part to arrive sums the parts fragment by
-// fragment in the order 0 .. ks-1, writes V, and returns the partials and the
-// counter to zero. Returns 1 (to all threads) if this workgroup completed V
-// of the tile.
+// at *split_counter and waits for the other parts. Then every part finishes
+// its own share of the fragments: it sums them over the parts in the order
+// 0 .. ks-1, writes those V entries and clears those fragments in every
+// part, so the tile's combine is spread over ks workgroups instead of
+// resting on one. A second count lets the last part out return the counter
+// to zero.
+//
+// The wait ends: the parts of a tile have consecutive workgroup ids,
+// workgroups are dispatched in id order, and at most one tile straddles the
+// dispatch front, with fewer parts than the device has slots, so every part
+// of a waiting tile is dispatched. If the bound runs
+// out all the same (a corrupt counter), the part skips its share and
+// returns 0. Returns 1 (to all threads) once this workgroup's V entries are
+// stored.
 template <int R, bool kCoherent, typename AkOf>
 __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
@@ -266,10 +324,19 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
     f32x4_t res[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) res[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < pl.n; ++q) {
-        const Piece pc = pl.p[q];
-        shrink_tile_mfma<R>(X, ak_of(pc.k), d_in, t0, pc.lo, pc.hi,
-                            ms0, ms1, sm, res);
+    // pieces two at a time: one pass over this part of d_in per pair
+    for (int q = 0; q < pl.n; q += kPassPieces) {
+        const Piece p0 = pl.p[q];
+        if (q + 1 < pl.n) {
+            const Piece p1 = pl.p[q + 1];
+            const bf16_t *const ak[2] = {ak_of(p0.k), ak_of(p1.k)};
+            const int lo[2] = {p0.lo, p1.lo}, hi[2] = {p0.hi, p1.hi};
+            shrink_tile_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res);
+        } else {
+            const bf16_t *const ak[1] = {ak_of(p0.k)};
+            const int lo[1] = {p0.lo}, hi[1] = {p0.hi};
+            shrink_tile_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res);
+        }
     }
     auto in_pieces = [&](int m) {
         bool in = false;
@@ -300,35 +367,32 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
 #pragma unroll
     for (int b = 0; b < NB; ++b)
         store4_coherent(rs, (uint32_t)kp * kTileBytes + (uint32_t)((wave * NB + b) * kWave + lane) * 16, res[b]);
-    if (!arrive_last(split_counter, (uint32_t)ks, s_flag)) return 0;
-    // NB fragments per thread. Every part of every fragment is requested
-    // before anything is summed or cleared: a load placed after a store to
-    // the same buffer would wait for it, which made the sum a chain of
-    // device-scope round trips.
+    publish(split_counter);
+    if (!wait_for(split_counter, (uint32_t)ks, s_flag)) return 0;
+    // This part's share: fragments [f0, f1), one per thread at most while
+    // kFrags / ks <= kBlock. Every part of a fragment is requested before it
+    // is summed or cleared: a load placed after a store to the same buffer
+    // would wait for that store.
     constexpr int kMaxParts = 8;
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t pv[NB][kMaxParts];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) pv[b][k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)((int)threadIdx.x + b * kBlock) * 16);
-    f32x4_t sum[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        sum[b] = zero;
+    const int f0 = kp * kFrags / ks, f1 = (kp + 1) * kFrags / ks;
+    for (int f = f0 + (int)threadIdx.x; f < f1; f += kBlock) {
+        f32x4_t pv[kMaxParts];
 #pragma unroll
         for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) sum[b] += pv[b][k];
+            if (k < ks) pv[k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16);
+        f32x4_t sum = zero;
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) sum += pv[k];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16, zero);
+        store_frag(f, sum);
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int k = 0; k < kMaxParts; ++k)
-            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)((int)threadIdx.x + b * kBlock) * 16, zero);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) store_frag((int)threadIdx.x + b * kBlock, sum[b]);
-    if (threadIdx.x == 0) __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every part has seen the full count once all of them have counted out
+    if (depart_last(split_counter, 2u * (uint32_t)ks, s_flag) && threadIdx.x == 0)
+        __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return 1;
 }
 
@@ -391,16 +455,19 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         __shared__ PieceList pl;
         __shared__ int s_flag;
         const int tiles = (M + kShrinkTileRows - 1) / kShrinkTileRows;
-        const int item = xcd_local_item(gemv_items, tiles * ks);
-        if (item < 0) return;
-        const int t = item / ks;
+        // parts of a tile have consecutive ids; with ks = 8, part kp of every
+        // tile runs on XCD kp (ids are dealt to the XCDs round-robin), where
+        // the tiles of a segment share slice kp of its A_k in one L2
+        const int t = ((int)blockIdx.x - gemv_items) / ks, kp = ((int)blockIdx.x - gemv_items) % ks;
+        if (t >= tiles) return;
         const int t0 = t * kShrinkTileRows;
         const MfmaAdapters ak_of(A_ptrs, num_adapters);
-        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
-                      min(t0 + kShrinkTileRows, M));
+        gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
+                             min(t0 + kShrinkTileRows, M));
         if (pl.n == 0) return;
         shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
-                                   item % ks, ks, ks > 1 ? counters + t : nullptr, partials, sm, &s_flag);
+                                   kp, ks, ks > 1 ? counters + (size_t)t * kCounterStride : nullptr,
+                                   partials, sm, &s_flag);
     }
 }
 
@@ -554,12 +621,22 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
-        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
-        for (int q = 0; q < pl.n; ++q) {
-            const Piece pc = pl.p[q];
-            const bf16_t *Bk = bk_of(pc.k);
-            expand_piece_mfma<R, true>(reinterpret_cast<bf16_t *>(Y), Bk, d_out, t0, pc.lo, pc.hi, n0, scale,
-                                 sm, [&](size_t idx) { return V[idx]; }, []() { return true; });
+        auto load_v4 = [&](size_t idx) { return *reinterpret_cast<const float4 *>(V + idx); };
+        auto ready = []() { return true; };
+        if constexpr (kMaxRB == 4) {  // a batch of long segments: most tiles have pieces
+            const SegPrefetch pre = prefetch_segments(seg_start, seg_adapter, num_segments);
+            expand_tile_mfma<R, true, true>(
+                reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
+                [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
+                bk_of, load_v4, ready);
+        } else {
+            expand_tile_mfma<R, true, false>(
+                reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
+                [&]() {
+                    gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
+                                         t0, t1);
+                },
+                bk_of, load_v4, ready);
         }
     }
 }
@@ -568,68 +645,6 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 // Fused: every shrink item (vector, then MFMA tiles) has a lower workgroup id
 // than every expand item (vector, then MFMA tiles).
 // ----------------------------------------------------------------------------
-
-// Thread 0 waits (bounded) until *counter reaches `target`. Returns 1 to
-// every thread of the workgroup on success; V loads issued after it see the
-// producers' V (device-scope atomics on both sides, see the top of the file).
-// The producers hold lower workgroup ids, were dispatched earlier and never
-// wait, so the wait ends; the bound only guards against a workspace whose
-// counters were not zero on entry.
-__device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag) {
-    if (threadIdx.x == 0) {
-        uint32_t spins = 0;
-        int ok = 1;
-        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(4);  // about 256 clocks between polls
-            if (++spins > (1u << 26)) {
-                ok = 0;
-                break;
-            }
-        }
-        *s_flag = ok;
-    }
-    __syncthreads();
-    return *s_flag;
-}
-
-// Publish this workgroup's V: every wave waits until its V stores (device-
-// scope atomics) have completed, then thread 0 increments the counter.
-__device__ __forceinline__ void publish(uint32_t *counter) {
-    wait_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Count this workgroup out; returns 1 to every thread if it was the last of
-// `expected` (all of them have finished reading V by then).
-__device__ __forceinline__ int depart_last(uint32_t *counter, uint32_t expected, int *s_flag) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = prev == expected - 1;
-    }
-    __syncthreads();
-    return *s_flag;
-}
-
-__device__ __forceinline__ void zero_rows(float *Vws, int lo, int hi, int R) {
-    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock) store_v<true>(Vws + (size_t)lo * R + i, 0.f);
-}
-
-__device__ __forceinline__ void zero_pairs(float *Vpairs, int lo, int hi, int R) {
-    uint64_t *p = reinterpret_cast<uint64_t *>(Vpairs) + (size_t)lo * R;
-    for (int i = threadIdx.x; i < (hi - lo) * R; i += kBlock)
-        __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
 
 // Row blocks of 4 in the fused kernel's vector expand keep its register
 // count low enough for two workgroups per CU (r <= 32), so that expand
@@ -643,13 +658,14 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int ks, float scale, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws, float *Vpairs,
-    float *partials) {
+    int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
+    float *Vpairs, float *partials) {
     // each segment and each 64-row tile owns one cache line of counters. A
     // segment's word 1 counts expand departures (the vector path hands V over
-    // as flagged pairs, Vpairs). A tile's word 0 says whether its V is
-    // complete (polled by the expand workgroups), word 1 counts departures,
-    // word 2 counts the parts of a split shrink.
+    // as flagged pairs, Vpairs). A tile's word 0 counts the shrink parts
+    // whose V entries are stored (polled by the expand workgroups until it
+    // reaches ks), word 1 counts expand departures, word 2 synchronises the
+    // parts of a split shrink.
     uint32_t *const seg_depart = seg_counters + 1;
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
@@ -660,7 +676,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const int tid = threadIdx.x;
     const int item = blockIdx.x;
     const int a0 = round_up_xcds(num_segments) * groups;  // vector shrink items
-    const int a1 = a0 + round_up_xcds(num_tiles * ks);    // MFMA shrink items (64 rows x part)
+    const int a1 = a0 + num_tiles * ks;                   // MFMA shrink items (64 rows x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -710,19 +726,16 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         } sm;
         __shared__ PieceList pl;
         const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
-        auto vload = [&](size_t idx) { return load_v<true>(Vws + idx); };
         if (item >= a0 && item < a1) {
-            // (64-row tile, part of d_in); the workgroup that completes the
-            // tile's V reports it on the tile's arrival word
-            const int it = xcd_local_item(a0, num_tiles * ks);
-            if (it < 0) return;
-            const int t = it / ks;
+            // (64-row tile, part of d_in); each part reports its share of
+            // the tile's V on the tile's arrival word
+            const int t = (item - a0) / ks, kp = (item - a0) % ks;
             const int t0 = t * kShrinkTileRows;
             const MfmaAdapters ak_of(A_ptrs, num_adapters);
-            gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
-                          min(t0 + kShrinkTileRows, M));
+            gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
+                                 t0, min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
-            if (shrink_mfma_item<R, true>(Vws, Xb, ak_of, pl, d_in, t, it % ks, ks,
+            if (shrink_mfma_item<R, true>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
                                           &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag))
                 publish(&tile_arrive[t * kCounterStride]);
             return;
@@ -734,20 +747,35 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
-        gather_pieces(pl, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1);
-        if (pl.n == 0) return;
-        // the shrink tile with the same rows reports once when its V is done
+        // the shrink tile with the same rows is done once all its parts report
         int state = -1;  // uniform: -1 not yet waited, else the result of the wait
         auto ready = [&]() {
-            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], 1u, &s_flag);
+            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], (uint32_t)ks, &s_flag);
             return state != 0;
         };
-        for (int q = 0; q < pl.n; ++q) {
-            const Piece pc = pl.p[q];
-            expand_piece_mfma<R, false>(reinterpret_cast<bf16_t *>(Y),
-                                 bk_of(pc.k), d_out, t0, pc.lo,
-                                 pc.hi, n0, scale, sm.expand, vload, ready);
+        // V of this tile's rows, read at device scope (written in this launch)
+        float *const vt = Vws + (size_t)t0 * R;
+        const __amdgpu_buffer_rsrc_t vr = coherent_rsrc(vt, (uint32_t)(kTileRows * R * sizeof(float)));
+        auto load_v4 = [&](size_t idx) {
+            const f32x4_t v = load4_coherent(vr, (uint32_t)((idx - (size_t)t0 * R) * sizeof(float)));
+            return make_float4(v[0], v[1], v[2], v[3]);
+        };
+        if (long_batch) {  // segments of 16 rows or more on average: most tiles have pieces
+            const SegPrefetch pre = prefetch_segments(seg_start, seg_adapter, num_segments);
+            expand_tile_mfma<R, false, true>(
+                reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
+                [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
+                bk_of, load_v4, ready);
+        } else {
+            expand_tile_mfma<R, false, false>(
+                reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
+                [&]() {
+                    gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
+                                         t0, t1);
+                },
+                bk_of, load_v4, ready);
         }
+        if (pl.n == 0) return;
         if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {
             for (int q = 0; q < pl.n; ++q) zero_rows(Vws, pl.p[q].lo, pl.p[q].hi, R);
             reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
@@ -774,7 +802,7 @@ template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const unsigned grid =
-        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)round_up_xcds(L.tiles * L.ks);
+        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)L.tiles * L.ks;
     char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
@@ -811,7 +839,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
-                          (unsigned)round_up_xcds(L.tiles * L.ks) +
+                          (unsigned)L.tiles * L.ks +
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(L.tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
@@ -819,7 +847,8 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.tiles, L.ks, a.scale, seg_c, tile_c,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.tiles, L.ks, a.scale,
+                       (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), seg_c, tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
                        reinterpret_cast<float *>(ws + L.partials));
     return hipGetLastError();

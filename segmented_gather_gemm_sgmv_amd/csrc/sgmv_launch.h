@@ -52,6 +52,8 @@ constexpr int kMacroSteps = 128;   // d_in elements per MFMA shrink macro step
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kCounterStride = 32;  // uint32 words per counter line (128 bytes)
+
 // How many workgroups split d_in for each 64-row MFMA shrink tile: enough for
 // about two workgroups per CU over the batch's tiles, at most 8 parts and at
 // least four 128-wide macro steps per part. One workgroup streams only a few
@@ -68,9 +70,9 @@ inline int shrink_ksplit(int M, int d_in) {
 }
 
 // Shrink workspace (bf16 only, when the split is more than one part): one
-// arrival counter per 64-row tile, then the tiles' partial results (tile x
-// part x 64 x max(r, 16) fp32: the MFMA tile is at least 16 columns wide).
-// Every launch leaves it all zero.
+// 128-byte counter line per 64-row tile (its parts arrived, then departed),
+// then the tiles' partial results (tile x part x 64 x max(r, 16) fp32: the
+// MFMA tile is at least 16 columns wide). Every launch leaves it all zero.
 struct ShrinkLayout {
     size_t counters, partials, total;
     int tiles, ks;
@@ -81,7 +83,7 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.counters = 0;
-    L.partials = align256(sizeof(uint32_t) * (size_t)L.tiles);
+    L.partials = align256(kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
     L.total = L.ks > 1 ? align256(L.partials + sizeof(float) * (size_t)L.tiles * L.ks *
                                                    kTileRows64 * (size_t)std::max(r, 16))
                        : 0;
@@ -94,8 +96,6 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
 // do not contend with another's; then V of the MFMA path (M x r fp32), the
 // split partials as above, and V of the vector path as M x r flagged 64-bit
 // pairs. Every launch leaves it all zero.
-constexpr int kCounterStride = 32;  // uint32 words per counter line
-
 struct FusedLayout {
     size_t seg_counters, tile_counters, v, partials, vpairs, total;
     int tiles, ks;

@@ -63,15 +63,17 @@ __device__ __forceinline__ int xcd_local_item(int first_id, int count) {
 __device__ __forceinline__ int clamp_to(int v, int M) { return v < 0 ? 0 : (v > M ? M : v); }
 
 // Number of offsets p in [0, num_segments] with clamp(seg_start[p]) <= t, by a
-// workgroup-wide search that tests 256 pivots per round (offsets are
-// non-decreasing). Every thread returns the same value.
-template <int kThreads>
-__device__ int count_starts_le(const int32_t *seg_start, int num_segments, int M, int t) {
+// workgroup-wide search that tests kBlockThreads pivots per round (offsets
+// are non-decreasing). With kPivot0 the first round's pivot of this thread,
+// offset tid * (num_segments / kBlockThreads + 1) clamped to num_segments,
+// comes in already loaded (`pivot0`). Every thread returns the same value.
+template <bool kPivot0>
+__device__ int count_starts_le(const int32_t *seg_start, int num_segments, int M, int t, int pivot0) {
     int base = 0, len = num_segments + 1;
-    while (len > 0) {
-        const int stride = (len + kThreads - 1) / kThreads;
+    for (int round = 0; len > 0; ++round) {
+        const int stride = (len + kBlockThreads - 1) / kBlockThreads;
         const int off = (int)threadIdx.x * stride;
-        const bool pred = off < len && clamp_to(seg_start[base + off], M) <= t;
+        const bool pred = off < len && clamp_to(kPivot0 && round == 0 ? pivot0 : seg_start[base + off], M) <= t;
         const int c = __syncthreads_count(pred);
         if (c == 0) break;
         const int last_true = base + (c - 1) * stride;
@@ -104,32 +106,75 @@ __device__ __forceinline__ void consider_segment(PieceList &pl, int s, int lo, i
     }
 }
 
+// Order LDS accesses across the workgroup without waiting for outstanding
+// global loads (a full barrier would also wait for every load in flight).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// This thread's entries of the segment metadata, requested as early as
+// possible (N >= 1 segments): the offset that is its first-round pivot in
+// count_starts_le, index min(tid * (N / kBlockThreads + 1), N), i.e. index
+// min(tid, N) when N < kBlockThreads, and adapter id min(tid, N - 1). Loads
+// return in issue order, so metadata requested before a tile's bulk loads
+// is not held up behind them.
+struct SegPrefetch {
+    int start, id;
+};
+
+__device__ __forceinline__ SegPrefetch prefetch_segments(const int32_t *seg_start,
+                                                         const int32_t *seg_adapter,
+                                                         int num_segments) {
+    // Kept here the same way as the adapter table loads: otherwise the
+    // compiler sinks them to their use, behind the tile's bulk loads.
+    // Global (not flat) loads: a flat load would make its consumer wait for
+    // the LDS counter too, and with it for every load in flight.
+    asm volatile("" : "+s"(seg_start), "+s"(seg_adapter));
+    typedef __attribute__((address_space(1))) const int32_t gconst_i32_t;
+    const int tid = threadIdx.x;
+    const int stride = num_segments / kBlockThreads + 1;
+    const SegPrefetch p{((gconst_i32_t *)seg_start)[min(tid * stride, num_segments)],
+                        ((gconst_i32_t *)seg_adapter)[min(tid, num_segments - 1)]};
+    asm volatile("" ::: "memory");
+    return p;
+}
+
 // Collect into `pl` the long segments (with a valid adapter) that intersect
 // rows [t0, t1) of the batch. With up to kBlockThreads - 1 segments all the
-// offsets and ids come in with one load per thread. Otherwise the segment
-// holding row t0 is found by a k-ary search and the offsets are scanned in
-// windows of kWave segments until one starts at or past t1. With valid
-// (non-decreasing) offsets at most five long segments meet a tile; pieces
-// beyond kMaxPieces (possible only with invalid offsets) are dropped. Call
-// with the whole workgroup; pl is visible to all threads on return.
-__device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int32_t *seg_adapter,
-                              int num_segments, int num_adapters, int M, int t0, int t1) {
+// offsets and ids come in with one load per thread (already in `pre` when
+// kPrefetched, and then the workgroup synchronises through LDS only,
+// leaving loads in flight). Otherwise the segment holding row t0 is found by
+// a k-ary search (its first round's pivots in `pre` when kPrefetched) and
+// the offsets are scanned in windows of kWave segments until one starts at
+// or past t1. With valid (non-decreasing) offsets at most five long segments
+// meet a tile; pieces beyond kMaxPieces (possible only with invalid offsets)
+// are dropped. Call with the whole workgroup; pl is visible to all threads
+// on return.
+template <bool kPrefetched>
+__device__ void gather_pieces(PieceList &pl, const SegPrefetch &pre, const int32_t *seg_start,
+                              const int32_t *seg_adapter, int num_segments, int num_adapters, int M,
+                              int t0, int t1) {
     const int tid = threadIdx.x;
     if (num_segments < kBlockThreads) {
         if (tid == 0) pl.n = 0;
-        if (tid <= num_segments) pl.starts[tid] = clamp_to(seg_start[tid], M);
-        if (tid < num_segments) pl.ids[tid] = seg_adapter[tid];
-        __syncthreads();
+        if (tid <= num_segments) pl.starts[tid] = clamp_to(kPrefetched ? pre.start : seg_start[tid], M);
+        if (tid < num_segments) pl.ids[tid] = kPrefetched ? pre.id : seg_adapter[tid];
+        if constexpr (kPrefetched)
+            lds_barrier();
+        else
+            __syncthreads();
         if (tid < num_segments) {
             const int lo = pl.starts[tid];
             consider_segment(pl, tid, lo, max(lo, pl.starts[tid + 1]), pl.ids[tid], num_adapters, t0, t1);
         }
-        __syncthreads();
+        lds_barrier();
         if (tid == 0 && pl.n > kMaxPieces) pl.n = kMaxPieces;
-        __syncthreads();
+        lds_barrier();
         return;
     }
-    const int cnt = count_starts_le<kBlockThreads>(seg_start, num_segments, M, t0);
+    const int cnt = count_starts_le<kPrefetched>(seg_start, num_segments, M, t0, pre.start);
     int first = cnt > 0 ? cnt - 1 : 0;
     if (tid == 0) pl.n = 0;
     while (true) {
@@ -162,17 +207,23 @@ __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int
 }
 
 // ----------------------------------------------------------------------------
-// Shrink tile: V[m, 0:R] = X[m, :] . A_k for the rows m in [p0, p1) of the
-// 64-row tile starting at t0, over macro steps [ms_begin, ms_end) of d_in
-// (kMacroK elements each). Wave w owns rows t0 + 16 w .. + 15 and all R
-// columns, so the waves share the A_k chunk of a macro step (R rows x
-// kMacroK): it is loaded once per workgroup, 16 lanes per 256-byte row chunk
-// (whole cache lines), and handed to the waves through LDS. X rows go
-// straight into registers: in slice q of a macro step, lane (i, g) brings
-// elements 32 q + 8 g .. + 7 of its row, and reads the same elements of A_k
-// rows 16 b + i from LDS. kStages macro steps are in flight per lane (a ring
-// of registers); LDS holds two A_k chunks, the one being read and the one
-// being written.
+// Shrink tile: V[m, 0:R] = X[m, :] . A_k for the rows m of up to two pieces
+// (segments, each with its own adapter) of the 64-row tile starting at t0,
+// over macro steps [ms_begin, ms_end) of d_in (kMacroK elements each). Wave w
+// owns rows t0 + 16 w .. + 15 and all R columns, so the waves share the A_k
+// chunk of a macro step (R rows x kMacroK): it is loaded once per workgroup,
+// 16 lanes per 256-byte row chunk (whole cache lines), and handed to the
+// waves through LDS. X rows go straight into registers: in slice q of a
+// macro step, lane (i, g) brings elements 32 q + 8 g .. + 7 of its row, and
+// reads the same elements of A_k rows 16 b + i from LDS. kStages macro steps
+// are in flight per lane (a ring of registers); LDS holds two A_k chunks per
+// piece, the one being read and the one being written.
+//
+// A tile that meets two segments takes both in one pass over d_in: X is
+// loaded once, both adapters' chunks are staged, and each wave multiplies
+// its rows by the adapter of every piece those rows touch, into one
+// accumulator set per piece. A row keeps the accumulator of its own piece,
+// so another adapter's values never reach it.
 //
 // LDS layout of an A_k chunk: row j occupies 16 slots of 16 bytes; element
 // chunk c (elements 8 c .. 8 c + 7 of the macro step) of row j sits in slot
@@ -182,37 +233,32 @@ __device__ void gather_pieces(PieceList &pl, const int32_t *seg_start, const int
 constexpr int kShrinkTileRows = 64;
 constexpr int kMacroK = 128;
 constexpr int kChunksPerRow = kMacroK * 2 / 16;   // 16-byte chunks per A_k row of a macro step
+constexpr int kPassPieces = 2;                    // pieces one pass over d_in can take
 
 template <int R>
 struct ShrinkSmem {
     static constexpr int kNB = R < 16 ? 1 : R / 16;                   // 16-column MFMA blocks
     static constexpr int kALoads = R * kChunksPerRow < kBlockThreads ? 1 : R * kChunksPerRow / kBlockThreads;
     static constexpr int kStages = R >= 64 ? 2 : (R >= 32 ? 3 : 4);   // macro steps in flight
-    uint4 a[2][R * kChunksPerRow];
+    uint4 a[2][kPassPieces][R * kChunksPerRow];
 };
 
-template <int R>
+template <int R, int NP>
 struct ShrinkStage {
-    uint4 a[ShrinkSmem<R>::kALoads];  // this thread's A_k chunks
-    uint4 x[4];                       // this lane's X elements, slices 0..3
-    uint32_t ok;                      // bits 0..3: X slice inside d_in; bits 4..: A chunk inside d_in
+    uint4 a[NP][ShrinkSmem<R>::kALoads];  // this thread's A_k chunks, per piece
+    uint4 x[4];                           // this lane's X elements, slices 0..3
+    uint32_t ok;                          // bits 0..3: X slice inside d_in; bits 4..: A chunk inside d_in
 };
 
-// Order LDS accesses across the workgroup without waiting for outstanding
-// global loads (a full barrier would also wait for every load in flight).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// On return, res[b][v] of lane (i, g) of wave w holds the tile's result for
-// row t0 + 16 w + 4 g + v and column 16 b + i (the MFMA D layout) wherever that
-// row lies in [p0, p1); elsewhere res is left as it was.
-template <int R>
-__device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int p0, int p1,
-                                 int ms_begin, int ms_end, ShrinkSmem<R> &sm,
-                                 f32x4_t (&res)[ShrinkSmem<R>::kNB]) {
+// Pieces lo[p] .. hi[p] - 1 (p < NP) are disjoint row ranges inside the tile,
+// Ak[p] their adapters. On return, res[b][v] of lane (i, g) of wave w holds
+// the tile's result for row t0 + 16 w + 4 g + v and column 16 b + i (the MFMA
+// D layout) wherever that row lies in a piece; elsewhere res is left as it
+// was.
+template <int R, int NP>
+__device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP], int d_in, int t0,
+                                 const int (&lo)[NP], const int (&hi)[NP], int ms_begin, int ms_end,
+                                 ShrinkSmem<R> &sm, f32x4_t (&res)[ShrinkSmem<R>::kNB]) {
     constexpr int NB = ShrinkSmem<R>::kNB;
     constexpr int kALoads = ShrinkSmem<R>::kALoads;
     constexpr int S = ShrinkSmem<R>::kStages;
@@ -223,14 +269,22 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, in
     const int g = lane >> 4;
     const int i = lane & 15;
     const int row = t0 + 16 * wave + i;
-    const bf16_t *xrow = X + (size_t)min(max(row, p0), p1 - 1) * d_in;  // rows outside: never stored
+    int rlo = lo[0], rhi = hi[0];
+    bool touches[NP];  // uniform per wave: the wave's 16 rows meet piece p
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        rlo = min(rlo, lo[p]);
+        rhi = max(rhi, hi[p]);
+        touches[p] = t0 + 16 * wave < hi[p] && t0 + 16 * wave + 16 > lo[p];
+    }
+    const bf16_t *xrow = X + (size_t)min(max(row, rlo), rhi - 1) * d_in;  // rows outside: never stored
     // Every step of the loop is straight-line: a step past ms_end (padding to
     // a multiple of S) or a slice past d_in loads a clamped address and its
     // operands are zeroed, never skipped, so each group of loads stays in
     // flight until its turn.
     const int niter = (ms_end - ms_begin + S - 1) / S * S;
 
-    auto load = [&](ShrinkStage<R> &st, int it) {
+    auto load = [&](ShrinkStage<R, NP> &st, int it) {
         const int ms = ms_begin + it;
         const bool step_ok = ms < ms_end;
         const int kb = max(0, min(ms, ms_end - 1)) * kMacroK;  // an empty range loads step 0
@@ -248,55 +302,68 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, in
             const int k = kb + 8 * (id % kChunksPerRow);
             const bool ok = step_ok && k < d_in;
             st.ok |= (uint32_t)ok << (4 + u);
-            st.a[u] = ld16(Ak + (size_t)(id / kChunksPerRow) * d_in + (ok ? k : d_in - 8));
+            const size_t off = (size_t)(id / kChunksPerRow) * d_in + (ok ? k : d_in - 8);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) st.a[p][u] = ld16(Ak[p] + off);
         }
     };
 
-    f32x4_t acc[NB];
+    f32x4_t acc[NP][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[p][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Consume one stage: its A_k chunks go to LDS buffer `buf`, then every
-    // wave multiplies its X slices with the whole chunk.
-    auto consume = [&](const ShrinkStage<R> &st, int buf) {
+    // wave multiplies its X slices with the chunk of each piece it touches.
+    auto consume = [&](const ShrinkStage<R, NP> &st, int buf) {
 #pragma unroll
         for (int u = 0; u < kALoads; ++u) {
             const int id = u * kBlockThreads + tid;
             if (id < kAChunks) {
                 const int j = id / kChunksPerRow;
                 const int c = id % kChunksPerRow;
-                const uint4 v = ((st.ok >> (4 + u)) & 1u) ? st.a[u] : make_uint4(0, 0, 0, 0);
-                sm.a[buf][j * kChunksPerRow + (c ^ (j & 15))] = v;
+                const bool ok = (st.ok >> (4 + u)) & 1u;
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    sm.a[buf][p][j * kChunksPerRow + (c ^ (j & 15))] = ok ? st.a[p][u] : make_uint4(0, 0, 0, 0);
             }
         }
         lds_barrier();
-        // The A operands of slice q + 1 are requested from LDS before the
-        // MFMAs of slice q are issued, so LDS latency overlaps the math
-        // instead of preceding every instruction.
-        auto lds_slice = [&](uint4 (&av)[NB], int q) {
+        uint4 xq[4];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int j = min(16 * b + i, R - 1);  // columns past R are never stored
-                av[b] = sm.a[buf][j * kChunksPerRow + ((4 * q + g) ^ (j & 15))];
+        for (int q = 0; q < 4; ++q) xq[q] = ((st.ok >> q) & 1u) ? st.x[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            if (NP > 1 && !touches[p]) continue;  // uniform
+            // The A operands of slice q + 1 are requested from LDS before
+            // the MFMAs of slice q are issued, so LDS latency overlaps the
+            // math instead of preceding every instruction.
+            auto lds_slice = [&](uint4 (&av)[NB], int q) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int j = min(16 * b + i, R - 1);  // columns past R are never stored
+                    av[b] = sm.a[buf][p][j * kChunksPerRow + ((4 * q + g) ^ (j & 15))];
+                }
+            };
+            uint4 av[2][NB];
+            lds_slice(av[0], 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q + 1 < 4) lds_slice(av[(q + 1) & 1], q + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[p][b] = mfma_bf16(as_bf16x8(xq[q]), as_bf16x8(av[q & 1][b]), acc[p][b]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        uint4 av[2][NB];
-        lds_slice(av[0], 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (q + 1 < 4) lds_slice(av[(q + 1) & 1], q + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            const uint4 xq = ((st.ok >> q) & 1u) ? st.x[q] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = mfma_bf16(as_bf16x8(xq), as_bf16x8(av[q & 1][b]), acc[b]);
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // The memory counter retires loads in issue order: scheduling barriers
     // keep each step's group of loads together, so consuming the oldest
     // group waits for that group only.
-    ShrinkStage<R> ring[S];
+    ShrinkStage<R, NP> ring[S];
 #pragma unroll
     for (int u = 0; u < S - 1; ++u) {
         load(ring[u], u);
@@ -316,9 +383,12 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, in
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int m = t0 + 16 * wave + 4 * g + v;
-        const bool in_piece = m >= p0 && m < p1;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) res[b][v] = in_piece ? acc[b][v] : res[b][v];
+        for (int p = 0; p < NP; ++p) {
+            const bool in_piece = m >= lo[p] && m < hi[p];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) res[b][v] = in_piece ? acc[p][b][v] : res[b][v];
+        }
     }
 }
 
@@ -362,15 +432,27 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// `ready()` is called by every thread once B and Y are on their way and
-// before V is read (a consumer of V produced in the same launch waits there);
-// if it returns false the piece is left untouched.
+// Expand tile: Y[m, n0:n0+128] += scale * V[m, :] . B_k[:, n0:n0+128] for
+// the rows m of every piece (segment with its adapter) of the 64-row tile
+// at t0. With kEarly the Y tile, and V when kVEarly, are requested before
+// the tile's pieces are known, so the segment metadata round trip overlaps
+// theirs (`gather()` collects the pieces into pl, from metadata the caller
+// requested before anything else). That pays when most tiles have pieces;
+// in a batch of short segments most tiles have none, and then the early
+// loads would be wasted, so without kEarly they wait for the pieces. Pieces
+// are taken one after another: each stages its B_k tile, updates its rows
+// of the Y tile held in registers, and the tile is stored once at the end.
+//
+// `ready()` is called by every thread once the first B tile is on its way
+// and before V is read (a consumer of V produced in the same launch waits
+// there); if it returns false the tile is left untouched.
 // kVEarly: V is final before the launch (a separate shrink), so it is
-// requested together with B instead of after the B tile is staged.
-template <int R, bool kVEarly, typename LoadV, typename Ready>
-__device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0, int p0, int p1,
-                                  int n0, float scale, ExpandSmem<R> &sm, LoadV load_v_fn,
-                                  Ready ready) {
+// requested together with Y.
+// load_v4(idx): V[idx .. idx + 3] (idx a multiple of 4).
+template <int R, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready>
+__device__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, float scale,
+                                 ExpandSmem<R> &sm, const PieceList &pl, Gather gather, BkOf bk_of,
+                                 LoadV4 load_v4, Ready ready) {
     constexpr int K = ExpandSmem<R>::kK;
     constexpr int KS = K / 32;                                   // MFMA steps over the rank
     constexpr int kBt = ExpandSmem<R>::kBtStride;
@@ -381,36 +463,42 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
     const int wave = tid / kWave;
     const int g = lane >> 4;
     const int i = lane & 15;
+    const int t1 = min(t0 + kTileRows, M);
 
-    // Y of this thread's output vectors, fetched early (each thread owns 4).
+    // The Y tile: each thread owns kYPer vectors of 8. Rows past the batch
+    // and columns past d_out load a clamped address and are never stored.
     constexpr int kYPer = kTileRows * kColVecs / kBlockThreads;
     uint4 yv[kYPer];
+    auto fetch_y = [&]() {
 #pragma unroll
-    for (int q = 0; q < kYPer; ++q) {
-        const int idx = tid + q * kBlockThreads;
-        const int m = t0 + idx / kColVecs;
-        const int n = n0 + (idx % kColVecs) * 8;
-        const bool ok = m >= p0 && m < p1 && n < d_out;
-        yv[q] = ld16(Y + (size_t)(ok ? m : p0) * d_out + (ok ? n : 0));  // others: never stored
-    }
+        for (int q = 0; q < kYPer; ++q) {
+            const int idx = tid + q * kBlockThreads;
+            const int m = min(t0 + idx / kColVecs, t1 - 1);
+            const int n = n0 + (idx % kColVecs) * 8;
+            yv[q] = ld16(Y + (size_t)m * d_out + (n < d_out ? n : 0));
+        }
+    };
 
     // V rows of this wave (A operand): lane (i, g) needs columns
     // ks * 32 + 8 g .. + 7 of row t0 + 16 w + i. Fetched raw first, then split
-    // into bf16 hi/lo halves once the values are needed.
-    const int row = t0 + 16 * wave + i;
-    const bool row_ok = row >= p0 && row < p1;
+    // into bf16 hi/lo halves once the values are needed. Rows outside the
+    // pieces are never stored; rank columns past R meet zero rows of the
+    // staged B tile but are zeroed anyway so a non-finite value cannot leak
+    // into a valid row.
+    const int vrow = min(t0 + 16 * wave + i, t1 - 1);
     float vraw[KS][8];
     auto fetch_v = [&]() {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // rows outside the piece are never stored; rank columns past R
-                // meet zero rows of the staged B tile but are zeroed anyway so
-                // a non-finite value cannot leak into a valid row
-                const int j = ks * 32 + 8 * g + e;
-                const float v = load_v_fn((size_t)(row_ok ? row : p0) * R + min(j, R - 1));
-                vraw[ks][e] = j < R ? v : 0.f;
+            for (int h = 0; h < 2; ++h) {
+                const int j = ks * 32 + 8 * g + 4 * h;
+                const float4 v = load_v4((size_t)vrow * R + min(j, R - 4));
+                const bool ok = j < R;
+                vraw[ks][4 * h + 0] = ok ? v.x : 0.f;
+                vraw[ks][4 * h + 1] = ok ? v.y : 0.f;
+                vraw[ks][4 * h + 2] = ok ? v.z : 0.f;
+                vraw[ks][4 * h + 3] = ok ? v.w : 0.f;
             }
     };
     bf16x8_t ahi[KS], alo[KS];
@@ -431,79 +519,99 @@ __device__ void expand_piece_mfma(bf16_t *Y, const bf16_t *Bk, int d_out, int t0
             alo[ks] = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
         }
     };
-    if constexpr (kVEarly) fetch_v();
-
-    // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
-    for (int idx = tid; idx < (R / 2) * kColVecs; idx += kBlockThreads) {
-        const int jp = idx / kColVecs;
-        const int c8 = idx % kColVecs;
-        const int n = n0 + c8 * 8 < d_out ? n0 + c8 * 8 : 0;  // columns past d_out are never stored
-        const uint4 r0 = ld16(Bk + (size_t)(2 * jp) * d_out + n);
-        const uint4 r1 = ld16(Bk + (size_t)(2 * jp + 1) * d_out + n);
-        const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-        const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+    if constexpr (kEarly) {
+        fetch_y();
+        if constexpr (kVEarly) fetch_v();
+        gather();
+    } else {
+        gather();
+        if (pl.n == 0) return;  // uniform
+        fetch_y();
+        if constexpr (kVEarly) fetch_v();
+    }
+    uint32_t touched = 0;  // bit q: Y vector q belongs to a piece
+    for (int pi = 0; pi < pl.n; ++pi) {
+        const Piece pc = pl.p[pi];
+        const bf16_t *Bk = bk_of(pc.k);
+        // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
+        for (int idx = tid; idx < (R / 2) * kColVecs; idx += kBlockThreads) {
+            const int jp = idx / kColVecs;
+            const int c8 = idx % kColVecs;
+            const int n = n0 + c8 * 8 < d_out ? n0 + c8 * 8 : 0;  // columns past d_out are never stored
+            const uint4 r0 = ld16(Bk + (size_t)(2 * jp) * d_out + n);
+            const uint4 r1 = ld16(Bk + (size_t)(2 * jp + 1) * d_out + n);
+            const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+            const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t lo16 = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-            const uint32_t hi16 = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
-            *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo16 = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
+                const uint32_t hi16 = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
+                *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
+            }
         }
-    }
-    if constexpr (R < K) {  // zero the padded part of the reduction
-        for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
-            sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
-    }
+        if constexpr (R < K) {  // zero the padded part of the reduction
+            for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
+                sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
+        }
+        if (pi == 0) {
+            if (!ready()) return;  // uniform
+            if constexpr (!kVEarly) fetch_v();
+            split_v();
+        }
+        __syncthreads();  // B tile in LDS
 
-    if (!ready()) return;  // uniform
-    if constexpr (!kVEarly) fetch_v();
-    split_v();
-    __syncthreads();  // B tile in LDS
-
-    // All B operands first, then eight independent accumulator chains, so
-    // neither LDS nor MFMA latency sits between consecutive instructions.
-    constexpr int NBLK = kExpandTileCols / 16;
-    uint4 bv[KS][NBLK];
+        // All B operands first, then eight independent accumulator chains, so
+        // neither LDS nor MFMA latency sits between consecutive instructions.
+        constexpr int NBLK = kExpandTileCols / 16;
+        uint4 bv[KS][NBLK];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b)
+                bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
+        f32x4_t acc[NBLK];
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(ahi[ks], as_bf16x8(bv[ks][b]), acc[b]);
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(alo[ks], as_bf16x8(bv[ks][b]), acc[b]);
+        }
+        __syncthreads();  // every wave is done with the B tile, whose LDS the delta tile reuses
 #pragma unroll
         for (int b = 0; b < NBLK; ++b)
-            bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
-    f32x4_t acc[NBLK];
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(ahi[ks], as_bf16x8(bv[ks][b]), acc[b]);
-#pragma unroll
-        for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(alo[ks], as_bf16x8(bv[ks][b]), acc[b]);
-    }
-    __syncthreads();  // every wave is done with the B tile, whose LDS the delta tile reuses
-#pragma unroll
-    for (int b = 0; b < NBLK; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[b][v];
-    __syncthreads();  // delta tile in LDS
+            for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[b][v];
+        __syncthreads();  // delta tile in LDS
 
+#pragma unroll
+        for (int q = 0; q < kYPer; ++q) {
+            const int idx = tid + q * kBlockThreads;
+            const int r = idx / kColVecs;
+            const int c8 = idx % kColVecs;
+            const int m = t0 + r;
+            if (m >= pc.lo && m < pc.hi) {
+                const float4 d0 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8]);
+                const float4 d1 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8 + 4]);
+                const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                float y[8];
+                widen<bf16_t>(yv[q], y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = y[e] + scale * d[e];
+                yv[q] = narrow<bf16_t>(y);
+                touched |= 1u << q;
+            }
+        }
+        __syncthreads();  // LDS free for the next piece
+    }
 #pragma unroll
     for (int q = 0; q < kYPer; ++q) {
         const int idx = tid + q * kBlockThreads;
-        const int r = idx / kColVecs;
-        const int c8 = idx % kColVecs;
-        const int m = t0 + r;
-        const int n = n0 + c8 * 8;
-        if (m >= p0 && m < p1 && n < d_out) {
-            const float4 d0 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8]);
-            const float4 d1 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8 + 4]);
-            const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            float y[8];
-            widen<bf16_t>(yv[q], y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = y[e] + scale * d[e];
-            st16(Y + (size_t)m * d_out + n, narrow<bf16_t>(y));
-        }
+        const int n = n0 + (idx % kColVecs) * 8;
+        if (((touched >> q) & 1u) && n < d_out) st16(Y + (size_t)(t0 + idx / kColVecs) * d_out + n, yv[q]);
     }
-    __syncthreads();  // LDS free for the next piece
 }
 
 }  // namespace sgmv

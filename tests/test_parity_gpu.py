@@ -366,3 +366,33 @@ def test_pool_table_boundaries(dev, oracle, P, dtype):
     assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
     assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, dtype))
     assert np.array_equal(bits(run_fused(c)), oracle_bits(oracle, Y_ref, dtype))
+
+
+@pytest.mark.parametrize("N,mean", [(255, 0.7), (256, 0.7), (257, 0.7), (1500, 0.7), (70000, 0.7),
+                                    (300, 20.0), (700, 20.0)])
+def test_many_segments_with_long_ones(dev, oracle, N, mean):
+    """Batches of many segments with a few long ones at the start, in the
+    middle and at the end. The MFMA tiles find their pieces in the segment
+    list by a search (one round for N < 256, several above); batches whose
+    segments average 16 rows or more request the search's first round before
+    anything else. mean 0.7: most segments empty or one row long; mean 20:
+    lengths spread over 0 .. 40. Integer inputs, bitwise, split and fused."""
+    rng = np.random.Generator(np.random.PCG64(80 + N))
+    if mean < 1:
+        lengths = rng.choice([0, 0, 0, 1, 1, 2], size=N)
+    else:
+        lengths = rng.integers(0, 41, size=N)
+    for pos, n in [(0, 40), (N // 3, 16), (N // 2, 100), (N - 1, 70)]:
+        lengths[pos] = n
+    ids = rng.integers(0, 7, size=N).astype(np.int32)
+    w = wl.Workload("many", int(lengths.sum()), 256, 264, 16, 32.0, torch.bfloat16, 7,
+                    wl.segments_from_lengths(lengths), ids)
+    assert (w.M >= 16 * N) == (mean > 1)
+    wl.fill_tensors(w, rng)
+    wl.integer_case(rng, w)
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    V, Y = run_split(c)
+    assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
+    assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, w.dtype))
+    assert np.array_equal(bits(run_fused(c)), oracle_bits(oracle, Y_ref, w.dtype))

@@ -396,3 +396,26 @@ def test_many_segments_with_long_ones(dev, oracle, N, mean):
     assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
     assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, w.dtype))
     assert np.array_equal(bits(run_fused(c)), oracle_bits(oracle, Y_ref, w.dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_mid_length_segments(dev, oracle, dtype):
+    """Batches whose segments average between 2 and 16 rows: vector segments
+    of 0 .. 15 rows (several row blocks each) mixed with one long segment,
+    integer inputs, bitwise, split and fused, and the workspace left zero."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    WS = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    for lengths in ([15, 1, 9, 0, 3, 12, 7, 2, 14, 5], [2, 2, 3, 2, 2], [13, 40, 1, 6, 11]):
+        ids = rng.integers(0, 6, size=len(lengths)).astype(np.int32)
+        w = wl.Workload("mid", int(sum(lengths)), 264, 2056, 16, 32.0, dtype, 6,
+                        wl.segments_from_lengths(lengths), ids)
+        assert 2 * len(lengths) <= w.M < 16 * len(lengths)
+        wl.fill_tensors(w, rng)
+        wl.integer_case(rng, w)
+        c = to_device(w, dev)
+        V_ref, Y_ref = oracle_run(oracle, w)
+        V, Y = run_split(c, workspace=WS)
+        assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
+        assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, dtype))
+        assert np.array_equal(bits(run_fused(c, workspace=WS)), oracle_bits(oracle, Y_ref, dtype))
+        assert int(torch.count_nonzero(WS)) == 0

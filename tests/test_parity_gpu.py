@@ -419,3 +419,48 @@ def test_mid_length_segments(dev, oracle, dtype):
         assert np.array_equal(bits(Y), oracle_bits(oracle, Y_ref, dtype))
         assert np.array_equal(bits(run_fused(c, workspace=WS)), oracle_bits(oracle, Y_ref, dtype))
         assert int(torch.count_nonzero(WS)) == 0
+
+
+def test_graph_replays(dev, oracle):
+    """The calls are stream-ordered and allocate nothing, so they can be
+    captured in a HIP graph. Replays of a captured fused call and of a
+    captured shrink + expand, with eager work and synchronisations between
+    replays, must each give the oracle's result bitwise (integer inputs) and
+    leave the workspace zero. A mixed batch: one-row, mid-length and long
+    segments, so the vector and MFMA paths and the split combine all run."""
+    rng = np.random.Generator(np.random.PCG64(95))
+    lengths = [1, 9, 130, 1, 3, 70, 15, 1]
+    ids = rng.integers(0, 6, size=len(lengths)).astype(np.int32)
+    w = wl.Workload("graph", int(sum(lengths)), 1024, 520, 16, 32.0, torch.bfloat16, 6,
+                    wl.segments_from_lengths(lengths), ids)
+    wl.fill_tensors(w, rng)
+    wl.integer_case(rng, w)
+    c = to_device(w, dev)
+    _, Y_ref = oracle_run(oracle, w)
+    want = oracle_bits(oracle, Y_ref, w.dtype)
+    WS = torch.zeros(sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype),
+                     dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(c.Y0)
+    V = torch.empty((w.M, w.r), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    graphs = {}
+    for name in ("fused", "split"):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            Y.copy_(c.Y0)
+            if name == "fused":
+                sg.sgmv_fused(Y, c.X, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha,
+                              workspace_buf=WS)
+            else:
+                sg.sgmv_shrink(V, c.X, c.A_ptrs, c.seg_start, c.seg_adapter, w.r, workspace_buf=WS)
+                sg.sgmv_expand(Y, V, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
+        graphs[name] = g
+    for rep in range(4):
+        for name, g in graphs.items():
+            Y.fill_(0)  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(Y), want), (name, rep)
+            assert int(torch.count_nonzero(WS)) == 0, (name, rep)

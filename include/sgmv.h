@@ -127,9 +127,52 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
                float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
                void *stream);
 
+/*
+ * Gathered forms: the batch stays in token order (Punica guide, figure "CUDA
+ * Threadblock Tiling": the block of a segment gathers that segment's rows of
+ * activations; section "Hardware-Level Optimizations in SGMV": grouping the
+ * requests by adapter, which these calls do through an index instead of
+ * moving X and Y).
+ *
+ * rows         device int32[M]: segment row p (p in [0, M), in segment order
+ *              exactly as seg_start describes it for the calls above) is
+ *              token row rows[p] of X and of Y. Normally the perm that
+ *              sgmv_build_segments returns, i.e. a permutation of [0, M).
+ * X, Y         token order, M rows each (same layout as above).
+ * V            segment order: V row p belongs to token rows[p], as in the
+ *              calls above.
+ *
+ * Each call computes what its contiguous counterpart computes on the batch
+ * gathered into segment order, with Y's rows put back at their tokens:
+ *     V[p, :]       = X[rows[p], :] . A_k                       (shrink_gather)
+ *     Y[rows[p], :] += (alpha / r) * V[p, :] . B_k             (expand_scatter)
+ *     Y[rows[p], :] += (alpha / r) * X[rows[p], :] . A_k . B_k  (fused_gather)
+ * Arguments, workspace, errors and the device-side defences are those of
+ * the contiguous call, plus: rows must not be NULL when M > 0. An entry of
+ * rows outside [0, M) makes segment row p absent: no Y row is written for
+ * it and V row p is unspecified (X is then read at row 0, never outside X).
+ * If two entries name the same token, that token's Y row is unspecified
+ * (the writes race); nothing outside the buffers is touched.
+ */
+int sgmv_shrink_gather(float *V, const void *X, const int32_t *rows, const uint64_t *A_ptrs,
+                       int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                       int32_t num_segments, int32_t M, int32_t d_in, int32_t r, int32_t dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+int sgmv_expand_scatter(void *Y, const float *V, const int32_t *rows, const uint64_t *B_ptrs,
+                        int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                        int32_t num_segments, int32_t M, int32_t d_out, int32_t r, float alpha,
+                        int32_t dtype, void *stream);
+
+int sgmv_fused_gather(void *Y, const void *X, const int32_t *rows, const uint64_t *A_ptrs,
+                      const uint64_t *B_ptrs, int32_t num_adapters, const int32_t *seg_start,
+                      const int32_t *seg_adapter, int32_t num_segments, int32_t M, int32_t d_in,
+                      int32_t d_out, int32_t r, float alpha, int32_t dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace sgmv_shrink and sgmv_fused need for these sizes; one
  * buffer of this size serves both (0 on invalid sizes, or when neither needs
- * any). */
+ * any). The gathered forms need the same. */
 size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
                             int32_t r, int32_t dtype);
 

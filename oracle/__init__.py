@@ -142,6 +142,40 @@ class Oracle:
         V = self.shrink(X, A_pool, seg_start, seg_adapter)
         return self.expand(Y_in, V, B_pool, seg_start, seg_adapter, alpha)
 
+    # -- the batch left in token order ---------------------------------------
+    # Punica guide, figure "CUDA Threadblock Tiling": a segment's block gathers
+    # the rows of activations that belong to it. Here the batch is not moved
+    # into segment order first: segment row p (rows seg_start[s] ..
+    # seg_start[s+1]-1 as above) is token row rows[p] of X and of Y.
+    @staticmethod
+    def _rows(rows, M: int) -> np.ndarray:
+        rows = np.asarray(rows, dtype=np.int64)
+        if rows.shape != (M,) or not np.array_equal(np.sort(rows), np.arange(M)):
+            raise ValueError("rows must be a permutation of 0 .. M-1")
+        return rows
+
+    def shrink_gather(self, X, A_pool, seg_start, seg_adapter, rows) -> np.ndarray:
+        """V[p] = X[rows[p]] . A_k for every segment row p (float64, M x r, in
+        segment order): the gathered rows of X, then the shrink above."""
+        X, _ = self._storage(X)
+        rows = self._rows(rows, X.shape[0])
+        return self.shrink(np.ascontiguousarray(X[rows]), A_pool, seg_start, seg_adapter)
+
+    def expand_scatter(self, Y_in, V, B_pool, seg_start, seg_adapter, rows, alpha: float) -> np.ndarray:
+        """Y[rows[p]] = Y_in[rows[p]] + (alpha / r) * V[p] . B_k (float64, token
+        order): the gathered rows of Y, the expand above, then each result put
+        back at its token row."""
+        rows = self._rows(rows, Y_in.shape[0])
+        Y = self.widen(Y_in) if Y_in.dtype != np.float64 else np.array(Y_in, dtype=np.float64)
+        Y[rows] = self.expand(np.ascontiguousarray(Y[rows]), V, B_pool, seg_start, seg_adapter, alpha)
+        return Y
+
+    def sgmv_gather(self, Y_in, X, A_pool, B_pool, seg_start, seg_adapter, rows,
+                    alpha: float) -> np.ndarray:
+        """Y[rows[p]] += (alpha / r) * X[rows[p]] . A_k . B_k (float64, token order)."""
+        V = self.shrink_gather(X, A_pool, seg_start, seg_adapter, rows)
+        return self.expand_scatter(Y_in, V, B_pool, seg_start, seg_adapter, rows, alpha)
+
     def round_bf16(self, y: np.ndarray) -> np.ndarray:
         """float64 -> bf16 bit patterns (uint16), nearest-even, one rounding."""
         y = np.ascontiguousarray(y, dtype=np.float64)

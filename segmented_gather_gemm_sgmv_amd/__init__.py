@@ -36,6 +36,12 @@ EXPORTS = {
     "sgmv_expand": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "sgmv_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _vp, _sz, _vp]),
+    "sgmv_shrink_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _vp, _sz, _vp]),
+    "sgmv_expand_scatter": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                           _i32, _vp]),
+    "sgmv_fused_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _i32, _vp, _sz, _vp]),
     "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
@@ -182,6 +188,70 @@ def sgmv_fused(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: t
     return Y
 
 
+def _rows_arg(rows: torch.Tensor, M: int) -> int:
+    if rows.numel() != M:
+        raise ValueError("rows must hold one entry per row of the batch")
+    return _dev(rows, "rows", torch.int32, 1)
+
+
+def sgmv_shrink_gather(V: torch.Tensor, X: torch.Tensor, rows: torch.Tensor, A_ptrs: torch.Tensor,
+                       seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int,
+                       workspace_buf: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """V[p] (fp32, segment order) = X[rows[p]] . A_k, with X in token order."""
+    M, d_in = X.shape
+    if V.shape != (M, r):
+        raise ValueError("V must be M x r")
+    need = sgmv_workspace_bytes(seg_adapter.numel(), M, d_in, d_in, r, X.dtype)
+    ws, ws_bytes = _workspace_args(workspace_buf, need, X, stream)
+    st = lib.sgmv_shrink_gather(_dev(V, "V", torch.float32, 2), _dev(X, "X", dim=2), _rows_arg(rows, M),
+                                _dev(A_ptrs, "A_ptrs", torch.int64, 1), A_ptrs.numel(),
+                                _dev(seg_start, "seg_start", torch.int32, 1),
+                                _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                                M, d_in, r, _dtype_code(X), ws, ws_bytes, _stream(X, stream))
+    _check("sgmv_shrink_gather", st)
+    return V
+
+
+def sgmv_expand_scatter(Y: torch.Tensor, V: torch.Tensor, rows: torch.Tensor, B_ptrs: torch.Tensor,
+                        seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int, alpha: float,
+                        stream=None) -> torch.Tensor:
+    """Y[rows[p]] += (alpha / r) * V[p] . B_k, with Y in token order (in place)."""
+    M, d_out = Y.shape
+    if V.shape != (M, r):
+        raise ValueError("V must be M x r")
+    st = lib.sgmv_expand_scatter(_dev(Y, "Y", dim=2), _dev(V, "V", torch.float32, 2), _rows_arg(rows, M),
+                                 _dev(B_ptrs, "B_ptrs", torch.int64, 1), B_ptrs.numel(),
+                                 _dev(seg_start, "seg_start", torch.int32, 1),
+                                 _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                                 M, d_out, r, float(alpha), _dtype_code(Y), _stream(Y, stream))
+    _check("sgmv_expand_scatter", st)
+    return Y
+
+
+def sgmv_fused_gather(Y: torch.Tensor, X: torch.Tensor, rows: torch.Tensor, A_ptrs: torch.Tensor,
+                      B_ptrs: torch.Tensor, seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int,
+                      alpha: float, workspace_buf: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Y[rows[p]] += (alpha / r) * X[rows[p]] . A_k . B_k in one launch, with X
+    and Y in token order (in place)."""
+    M, d_in = X.shape
+    M2, d_out = Y.shape
+    if M2 != M:
+        raise ValueError("X and Y must have the same number of rows")
+    if A_ptrs.numel() != B_ptrs.numel():
+        raise ValueError("A_ptrs and B_ptrs must have one entry per adapter")
+    need = sgmv_workspace_bytes(seg_adapter.numel(), M, d_in, d_out, r, X.dtype)
+    ws, ws_bytes = _workspace_args(workspace_buf, need, X, stream)
+    st = lib.sgmv_fused_gather(_dev(Y, "Y", dim=2), _dev(X, "X", dim=2), _rows_arg(rows, M),
+                               _dev(A_ptrs, "A_ptrs", torch.int64, 1), _dev(B_ptrs, "B_ptrs", torch.int64, 1),
+                               A_ptrs.numel(), _dev(seg_start, "seg_start", torch.int32, 1),
+                               _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                               M, d_in, d_out, r, float(alpha), _dtype_code(X), ws, ws_bytes,
+                               _stream(X, stream))
+    _check("sgmv_fused_gather", st)
+    return Y
+
+
 def sgmv_build_segments(token_adapter) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Host: group tokens by adapter. Returns (perm, seg_start, seg_adapter)."""
     ids = np.ascontiguousarray(np.asarray(token_adapter, dtype=np.int32))
@@ -217,6 +287,7 @@ def sgmv_version() -> int:
     return int(lib.sgmv_version())
 
 
-__all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_workspace_bytes", "sgmv_build_segments",
+__all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sgmv_expand_scatter",
+           "sgmv_fused_gather", "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16"]

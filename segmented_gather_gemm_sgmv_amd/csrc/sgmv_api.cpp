@@ -35,7 +35,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; 
 
 extern "C" {
 
-int sgmv_version(void) { return 100; }
+int sgmv_version(void) { return 200; }
 
 const char *sgmv_status_string(int status) {
     switch (status) {
@@ -70,41 +70,48 @@ int check_workspace(const void *workspace, size_t workspace_bytes, size_t need) 
 }
 }  // namespace
 
-int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
-                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
-                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *workspace,
+}  // extern "C"
+
+namespace {
+
+// The checks and launches shared by the contiguous calls (rows == NULL,
+// gathered == false) and the gathered ones (rows required when M > 0).
+int shrink_call(float *V, const void *X, const int32_t *rows, bool gathered, const uint64_t *A_ptrs,
+                int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                int32_t num_segments, int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *workspace,
                 size_t workspace_bytes, void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
     if (!valid_dim(d_in) || (int64_t)M * d_in > kMaxElems) return SGMV_ERR_SHAPE;
     if (M == 0 || num_segments == 0) return SGMV_OK;
-    if (!V || !X || !A_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!V || !X || !A_ptrs || !seg_start || !seg_adapter || (gathered && !rows)) return SGMV_ERR_NULL;
     if (!aligned16(V) || !aligned16(X)) return SGMV_ERR_ALIGN;
     st = check_workspace(workspace, workspace_bytes, sgmv::shrink_layout(M, d_in, r, dtype).total);
     if (st != SGMV_OK) return st;
     sgmv::ShrinkArgs a{V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                       num_segments, M, d_in, r, dtype, workspace};
+                       num_segments, M, d_in, r, dtype, workspace, gathered ? rows : nullptr};
     return hip_status(sgmv::launch_shrink(a, static_cast<hipStream_t>(stream)));
 }
 
-int sgmv_expand(void *Y, const float *V, const uint64_t *B_ptrs, int32_t num_adapters,
-                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
-                int32_t M, int32_t d_out, int32_t r, float alpha, int32_t dtype, void *stream) {
+int expand_call(void *Y, const float *V, const int32_t *rows, bool gathered, const uint64_t *B_ptrs,
+                int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                int32_t num_segments, int32_t M, int32_t d_out, int32_t r, float alpha, int32_t dtype,
+                void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
     if (!valid_dim(d_out) || (int64_t)M * d_out > kMaxElems) return SGMV_ERR_SHAPE;
     if (M == 0 || num_segments == 0) return SGMV_OK;
-    if (!Y || !V || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!Y || !V || !B_ptrs || !seg_start || !seg_adapter || (gathered && !rows)) return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(V)) return SGMV_ERR_ALIGN;
     sgmv::ExpandArgs a{Y, V, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments,
-                       M, d_out, r, dtype, alpha / (float)r};
+                       M, d_out, r, dtype, alpha / (float)r, gathered ? rows : nullptr};
     return hip_status(sgmv::launch_expand(a, static_cast<hipStream_t>(stream)));
 }
 
-int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
-               int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
-               int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
-               float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+int fused_call(void *Y, const void *X, const int32_t *rows, bool gathered, const uint64_t *A_ptrs,
+               const uint64_t *B_ptrs, int32_t num_adapters, const int32_t *seg_start,
+               const int32_t *seg_adapter, int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
+               int32_t r, float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
                void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
@@ -112,14 +119,69 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
         (int64_t)M * d_out > kMaxElems)
         return SGMV_ERR_SHAPE;
     if (M == 0 || num_segments == 0) return SGMV_OK;
-    if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter || (gathered && !rows))
+        return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
     st = check_workspace(workspace, workspace_bytes,
                          sgmv::fused_layout(num_segments, M, d_in, r, dtype).total);
     if (st != SGMV_OK) return st;
     sgmv::FusedArgs a{Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
-                      num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, workspace};
+                      num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, workspace,
+                      gathered ? rows : nullptr};
     return hip_status(sgmv::launch_fused(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgmv_shrink(float *V, const void *X, const uint64_t *A_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_in, int32_t r, int32_t dtype, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return shrink_call(V, X, nullptr, false, A_ptrs, num_adapters, seg_start, seg_adapter, num_segments,
+                       M, d_in, r, dtype, workspace, workspace_bytes, stream);
+}
+
+int sgmv_expand(void *Y, const float *V, const uint64_t *B_ptrs, int32_t num_adapters,
+                const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                int32_t M, int32_t d_out, int32_t r, float alpha, int32_t dtype, void *stream) {
+    return expand_call(Y, V, nullptr, false, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments,
+                       M, d_out, r, alpha, dtype, stream);
+}
+
+int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+               int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+               int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
+               float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+               void *stream) {
+    return fused_call(Y, X, nullptr, false, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
+                      num_segments, M, d_in, d_out, r, alpha, dtype, workspace, workspace_bytes, stream);
+}
+
+int sgmv_shrink_gather(float *V, const void *X, const int32_t *rows, const uint64_t *A_ptrs,
+                       int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                       int32_t num_segments, int32_t M, int32_t d_in, int32_t r, int32_t dtype,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    return shrink_call(V, X, rows, true, A_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
+                       d_in, r, dtype, workspace, workspace_bytes, stream);
+}
+
+int sgmv_expand_scatter(void *Y, const float *V, const int32_t *rows, const uint64_t *B_ptrs,
+                        int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                        int32_t num_segments, int32_t M, int32_t d_out, int32_t r, float alpha,
+                        int32_t dtype, void *stream) {
+    return expand_call(Y, V, rows, true, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
+                       d_out, r, alpha, dtype, stream);
+}
+
+int sgmv_fused_gather(void *Y, const void *X, const int32_t *rows, const uint64_t *A_ptrs,
+                      const uint64_t *B_ptrs, int32_t num_adapters, const int32_t *seg_start,
+                      const int32_t *seg_adapter, int32_t num_segments, int32_t M, int32_t d_in,
+                      int32_t d_out, int32_t r, float alpha, int32_t dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return fused_call(Y, X, rows, true, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
+                      num_segments, M, d_in, d_out, r, alpha, dtype, workspace, workspace_bytes, stream);
 }
 
 int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,

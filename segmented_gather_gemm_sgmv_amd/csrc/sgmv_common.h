@@ -144,6 +144,31 @@ struct AdapterTable<false> {
     __device__ __forceinline__ uint64_t address(const uint64_t *ptrs, int k) const { return ptrs[k]; }
 };
 
+// Token row of segment-ordered row p. The contiguous calls take the batch in
+// segment order (p itself); the gathered calls take it in token order
+// through an index, rows[p]. An index outside [0, M) is read as row 0 and
+// reported with ok = false: its Y row is never stored.
+template <bool kGather>
+struct RowMap {
+    static constexpr bool kIndexed = kGather;
+    const int32_t *rows;
+    int M;
+    __device__ __forceinline__ int operator()(int p, bool &ok) const {
+        if constexpr (kGather) {
+            const int q = rows[p];
+            ok = (unsigned)q < (unsigned)M;
+            return ok ? q : 0;
+        } else {
+            ok = true;
+            return p;
+        }
+    }
+    __device__ __forceinline__ int operator()(int p) const {
+        bool ok;
+        return (*this)(p, ok);
+    }
+};
+
 // Segment bounds clamped into [0, M]; an inverted pair is an empty segment.
 __device__ __forceinline__ void segment_rows(const int32_t *seg_start, int s, int M, int &lo,
                                              int &hi) {

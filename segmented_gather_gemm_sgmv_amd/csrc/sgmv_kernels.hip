@@ -112,9 +112,9 @@ __device__ __forceinline__ bool poll_v_block(const float *V, int row0, int nrows
 // the block repeat the last row and are simply not stored. Straight-line
 // loads let the compiler keep all of them in flight at once.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int ROWS, bool kFlagged, typename ArowFn>
+template <typename T, int R, int ROWS, bool kFlagged, typename ArowFn, typename RM>
 __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
-                                            int row0, int nrows, int j, int lane) {
+                                            int row0, int nrows, int j, int lane, RM rm) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int U = ROWS <= 2 ? kShrinkUnroll : (ROWS <= 4 ? kShrinkUnroll / 2 : kShrinkUnroll / 4);
     const int nvec = d_in / VEC;
@@ -123,7 +123,7 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
         acc[m] = 0.f;
-        xrow[m] = X + (size_t)(row0 + min(m, nrows - 1)) * d_in;
+        xrow[m] = X + (size_t)rm(row0 + min(m, nrows - 1)) * d_in;
     }
 
     const T *Arow = nullptr;
@@ -177,20 +177,21 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
 }
 
 // All rows of one segment, rank row j, one wave. `arow_fn()` returns the
-// address of row j of the segment's A_k.
-template <typename T, int R, bool kFlagged, typename ArowFn>
+// address of row j of the segment's A_k; rm(p) the row of X behind segment
+// row p.
+template <typename T, int R, bool kFlagged, typename ArowFn, typename RM>
 __device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
-                                                    int lo, int hi, int j, int lane) {
+                                                    int lo, int hi, int j, int lane, RM rm) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            shrink_wave<T, R, 1, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 1, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
         else if (nrows <= 2)
-            shrink_wave<T, R, 2, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 2, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
         else if (nrows <= 4)
-            shrink_wave<T, R, 4, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 4, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
         else
-            shrink_wave<T, R, 8, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane);
+            shrink_wave<T, R, 8, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
     }
 }
 
@@ -211,11 +212,11 @@ __device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_ad
 // One vector-path shrink item: rank row j of segment s, one wave. Returns
 // false if the segment is empty, names no valid adapter or belongs to the
 // MFMA path (then nothing is written).
-template <typename T, int R, bool kFlagged, bool kSpec>
+template <typename T, int R, bool kFlagged, bool kSpec, typename RM>
 __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int j, int M,
-                                                   int d_in, int lane) {
+                                                   int d_in, int lane, RM rm) {
     AdapterTable<kSpec> tab;
     tab.load(A_ptrs, num_adapters, lane);
     int lo, hi;
@@ -223,7 +224,7 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     segment_rows(seg_start, s, M, lo, hi);
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
-    shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane);
+    shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane, rm);
     return true;
 }
 
@@ -308,11 +309,11 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
 // out all the same (a corrupt counter), the part skips its share and
 // returns 0. Returns 1 (to all threads) once this workgroup's V entries are
 // stored.
-template <int R, bool kCoherent, typename AkOf>
+template <int R, bool kCoherent, typename AkOf, typename RM>
 __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
                                 uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
-                                int *s_flag) {
+                                int *s_flag, RM rm) {
     constexpr int NB = ShrinkSmem<R>::kNB;
     constexpr int kFrags = kWavesPerBlock * NB * kWave;  // 16-byte fragments per partial tile
     constexpr uint32_t kTileBytes = kFrags * 16;
@@ -331,11 +332,11 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
             const Piece p1 = pl.p[q + 1];
             const bf16_t *const ak[2] = {ak_of(p0.k), ak_of(p1.k)};
             const int lo[2] = {p0.lo, p1.lo}, hi[2] = {p0.hi, p1.hi};
-            shrink_tile_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res);
+            shrink_tile_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
         } else {
             const bf16_t *const ak[1] = {ak_of(p0.k)};
             const int lo[1] = {p0.lo}, hi[1] = {p0.hi};
-            shrink_tile_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res);
+            shrink_tile_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
         }
     }
     auto in_pieces = [&](int m) {
@@ -428,12 +429,12 @@ struct MfmaAdapters {
 // Items [0, round_up_xcds(N) * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
 // one per (64-row tile, part of d_in) (bf16 only).
-template <typename T, int R>
+template <typename T, int R, bool kGather>
 __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
     const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int ks,
-    uint32_t *counters, float *partials) {
+    uint32_t *counters, float *partials, RowMap<kGather> rm) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = round_up_xcds(num_segments) * groups;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -444,10 +445,10 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         const int lane = threadIdx.x & (kWave - 1);
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, false, true>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, lane);
+                                                  s, j, M, d_in, lane, rm);
         else
             shrink_vector_item<T, R, false, false>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                   s, j, M, d_in, lane);
+                                                   s, j, M, d_in, lane, rm);
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -467,28 +468,32 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         if (pl.n == 0) return;
         shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
                                    kp, ks, ks > 1 ? counters + (size_t)t * kCounterStride : nullptr,
-                                   partials, sm, &s_flag);
+                                   partials, sm, &s_flag, rm);
     }
 }
 
 // ----------------------------------------------------------------------------
 // Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready>
+template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready, typename RM>
 __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
-                                            int nrows, int n0, bool active, float scale, Ready ready) {
+                                            int nrows, int n0, bool active, float scale, Ready ready,
+                                            RM rm) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     // Loads are unconditional (see shrink_wave): an inactive lane reads
     // column 0, rows past the block repeat the last row; neither is stored.
     const int nc = active ? n0 : 0;
-    int rowc[RB];
+    int rowc[RB];   // segment rows (V)
+    int yrow[RB];   // their rows of Y
+    bool yok[RB];   // yrow may be stored
     uint4 yv[RB];
     float acc[RB][VEC];
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
         rowc[m] = row0 + min(m, nrows - 1);
-        yv[m] = ld16(Y + (size_t)rowc[m] * d_out + nc);
+        yrow[m] = rm(rowc[m], yok[m]);
+        yv[m] = ld16(Y + (size_t)yrow[m] * d_out + nc);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[m][e] = 0.f;
     }
@@ -535,12 +540,13 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
     if (!active) return;
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
-        if (m < nrows) {
+        if (m < nrows && yok[m]) {
             float y[VEC];
             widen<T>(yv[m], y);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] + scale * acc[m][e];
-            st16(Y + (size_t)(row0 + m) * d_out + n0, narrow<T>(y));
+            // (contiguous: the same row, row0 + m, in the form the compiler had before)
+            st16(Y + (size_t)(RM::kIndexed ? yrow[m] : row0 + m) * d_out + n0, narrow<T>(y));
         }
     }
 }
@@ -550,20 +556,21 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
 // before V is read; the rows are left untouched if it returns false. Rows
 // are taken kMaxRB (4 or 8) at a time: 8 reads B_k half as often, 4 needs
 // about 80 fewer registers per lane.
-template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready>
+template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready, typename RM>
 __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn, int d_out, int lo,
-                                               int hi, int n0, bool active, float scale, Ready ready) {
+                                               int hi, int n0, bool active, float scale, Ready ready,
+                                               RM rm) {
     static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
     for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
         const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
         else if (kMaxRB == 4 || nrows <= 4)
-            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
         else if constexpr (kMaxRB == 8)
-            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready);
+            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
     }
 }
 
@@ -571,19 +578,19 @@ __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn,
 // segment s; `ready` as for expand_segment. Returns false if the segment is
 // empty, names no valid adapter or belongs to the MFMA path. lo, hi receive
 // the segment's rows.
-template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn>
+template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn, typename RM>
 __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int n0, int M,
                                                    int d_out, float scale, int &lo, int &hi,
-                                                   ReadyFn ready) {
+                                                   ReadyFn ready, RM rm) {
     AdapterTable<kSpec> tab;
     tab.load(B_ptrs, num_adapters, threadIdx.x & (kWave - 1));
     const int k = seg_adapter[s];
     segment_rows(seg_start, s, M, lo, hi);
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
-    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready);
+    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm);
     return true;
 }
 
@@ -592,12 +599,12 @@ __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const u
 // segments the MFMA path owns. Items after that: MFMA tiles of kTileRows
 // batch rows by kExpandTileCols columns (bf16 only). kMaxRB: rows per block
 // of the vector path (see expand_segment).
-template <typename T, int R, int kMaxRB>
+template <typename T, int R, int kMaxRB, bool kGather>
 __global__ __launch_bounds__(kBlock) void expand_kernel(
     T *__restrict__ Y, const float *__restrict__ V, const uint64_t *__restrict__ B_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
     const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_out, int ntiles_g,
-    int ntiles_m, float scale) {
+    int ntiles_m, float scale, RowMap<kGather> rm) {
     constexpr int VEC = Elem<T>::kPerVec;
     const int gemv_items = num_segments * ntiles_g;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -609,7 +616,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         // B_k's address is loaded once the id is known: reading the table
         // early measured slower here, where Y is requested alongside B
         expand_vector_item<T, R, false, kMaxRB, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter,
-                                                       s, n0, M, d_out, scale, lo, hi, []() { return true; });
+                                                       s, n0, M, d_out, scale, lo, hi, []() { return true; }, rm);
         return;
     }
     if constexpr (Elem<T>::kIsBf16) {
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
             expand_tile_mfma<R, true, true>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
                 [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
-                bk_of, load_v4, ready);
+                bk_of, load_v4, ready, rm);
         } else {
             expand_tile_mfma<R, true, false>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
                     gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
                                          t0, t1);
                 },
-                bk_of, load_v4, ready);
+                bk_of, load_v4, ready, rm);
         }
     }
 }
@@ -652,14 +659,14 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 // workgroups still run.
 constexpr int kFusedRB = 4;
 
-template <typename T, int R>
+template <typename T, int R, bool kGather>
 __global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
     int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials) {
+    float *Vpairs, float *partials, RowMap<kGather> rm) {
     // each segment and each 64-row tile owns one cache line of counters. A
     // segment's word 1 counts expand departures (the vector path hands V over
     // as flagged pairs, Vpairs). A tile's word 0 counts the shrink parts
@@ -686,10 +693,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
         const int j = grp * kWavesPerBlock + tid / kWave;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                 s, j, M, d_in, tid & (kWave - 1));
+                                                 s, j, M, d_in, tid & (kWave - 1), rm);
         else
             shrink_vector_item<T, R, true, false>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, tid & (kWave - 1));
+                                                  s, j, M, d_in, tid & (kWave - 1), rm);
         return;
     }
     if (item >= a1 && item < a2) {
@@ -705,10 +712,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             num_adapters <= kSpecTable
                 ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
                                                                  seg_adapter, s, n0, M, d_out, scale,
-                                                                 lo, hi, ready)
+                                                                 lo, hi, ready, rm)
                 : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
                                                                   seg_adapter, s, n0, M, d_out, scale,
-                                                                  lo, hi, ready);
+                                                                  lo, hi, ready, rm);
         if (!valid) return;
         if (depart_last(&seg_depart[s * kCounterStride], (uint32_t)ntiles_g, &s_flag)) {
             // last one out: return the segment's V pairs and its counter to zero
@@ -736,7 +743,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
                                  t0, min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
             if (shrink_mfma_item<R, true>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
-                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag))
+                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag, rm))
                 publish(&tile_arrive[t * kCounterStride]);
             return;
         }
@@ -765,7 +772,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             expand_tile_mfma<R, false, true>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
                 [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
-                bk_of, load_v4, ready);
+                bk_of, load_v4, ready, rm);
         } else {
             expand_tile_mfma<R, false, false>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
@@ -773,7 +780,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
                     gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
                                          t0, t1);
                 },
-                bk_of, load_v4, ready);
+                bk_of, load_v4, ready, rm);
         }
         if (pl.n == 0) return;
         if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {
@@ -798,22 +805,28 @@ static int gemv_col_tiles(int d_out) {
     return (d_out + cols - 1) / cols;
 }
 
-template <typename T, int R>
-static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
+template <typename T, int R, bool kGather>
+static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const unsigned grid =
         (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)L.tiles * L.ks;
     char *ws = static_cast<char *>(a.workspace);
-    hipLaunchKernelGGL((shrink_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st, a.V,
+    hipLaunchKernelGGL((shrink_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
                        a.seg_adapter, a.num_segments, a.M, a.d_in, L.ks,
                        L.ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
-                       L.ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr);
+                       L.ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr,
+                       RowMap<kGather>{a.rows, a.M});
     return hipGetLastError();
 }
 
 template <typename T, int R>
-static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
+static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
+    return a.rows ? launch_shrink_g<T, R, true>(a, st) : launch_shrink_g<T, R, false>(a, st);
+}
+
+template <typename T, int R, bool kGather>
+static hipError_t launch_expand_g(const ExpandArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int tiles = mfma_tiles(a.dtype, a.M);
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
@@ -822,19 +835,25 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
     // vector path: rows 8 at a time read B_k half as often. Batches of long
     // segments run mostly on the MFMA path, whose occupancy the vector path's
     // registers would otherwise limit: rows 4 at a time.
+    const RowMap<kGather> rm{a.rows, a.M};
     if ((int64_t)a.M < 16 * (int64_t)a.num_segments)
-        hipLaunchKernelGGL((expand_kernel<T, R, 8>), dim3(grid), dim3(kBlock), 0, st,
+        hipLaunchKernelGGL((expand_kernel<T, R, 8, kGather>), dim3(grid), dim3(kBlock), 0, st,
                            reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
-                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
+                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale, rm);
     else
-        hipLaunchKernelGGL((expand_kernel<T, R, 4>), dim3(grid), dim3(kBlock), 0, st,
+        hipLaunchKernelGGL((expand_kernel<T, R, 4, kGather>), dim3(grid), dim3(kBlock), 0, st,
                            reinterpret_cast<T *>(a.Y), a.V, a.B_ptrs, a.num_adapters, a.seg_start,
-                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale);
+                           a.seg_adapter, a.num_segments, a.M, a.d_out, ntiles_g, ntiles_m, a.scale, rm);
     return hipGetLastError();
 }
 
 template <typename T, int R>
-static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
+static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
+    return a.rows ? launch_expand_g<T, R, true>(a, st) : launch_expand_g<T, R, false>(a, st);
+}
+
+template <typename T, int R, bool kGather>
+static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
     const FusedLayout L = fused_layout(a.num_segments, a.M, a.d_in, a.r, a.dtype);
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
@@ -844,14 +863,19 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
-    hipLaunchKernelGGL((fused_kernel<T, R>), dim3(grid), dim3(kBlock), 0, st,
+    hipLaunchKernelGGL((fused_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
                        a.d_in, a.d_out, ntiles_g, ntiles_m, L.tiles, L.ks, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), seg_c, tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
-                       reinterpret_cast<float *>(ws + L.partials));
+                       reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M});
     return hipGetLastError();
+}
+
+template <typename T, int R>
+static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
+    return a.rows ? launch_fused_g<T, R, true>(a, st) : launch_fused_g<T, R, false>(a, st);
 }
 
 #define SGMV_RANK_SWITCH(FN, T, args, st)           \

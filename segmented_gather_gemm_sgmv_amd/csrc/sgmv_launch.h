@@ -21,6 +21,7 @@ struct ShrinkArgs {
     const int32_t *seg_adapter;
     int num_segments, M, d_in, r, dtype;
     void *workspace;
+    const int32_t *rows = nullptr;  // gathered call: token row of each segment row
 };
 
 struct ExpandArgs {
@@ -32,6 +33,7 @@ struct ExpandArgs {
     const int32_t *seg_adapter;
     int num_segments, M, d_out, r, dtype;
     float scale;
+    const int32_t *rows = nullptr;  // scattered call: token row of each segment row
 };
 
 struct FusedArgs {
@@ -45,6 +47,7 @@ struct FusedArgs {
     int num_segments, M, d_in, d_out, r, dtype;
     float scale;
     void *workspace;
+    const int32_t *rows = nullptr;  // gathered call: token row of each segment row
 };
 
 constexpr int kTileRows64 = 64;    // rows of an MFMA shrink or expand tile (and of a fused handoff)

@@ -251,14 +251,14 @@ struct ShrinkStage {
 };
 
 // Pieces lo[p] .. hi[p] - 1 (p < NP) are disjoint row ranges inside the tile,
-// Ak[p] their adapters. On return, res[b][v] of lane (i, g) of wave w holds
+// Ak[p] their adapters; rm maps a segment row to the row of X it reads. On return, res[b][v] of lane (i, g) of wave w holds
 // the tile's result for row t0 + 16 w + 4 g + v and column 16 b + i (the MFMA
 // D layout) wherever that row lies in a piece; elsewhere res is left as it
 // was.
-template <int R, int NP>
+template <int R, int NP, typename RM>
 __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP], int d_in, int t0,
                                  const int (&lo)[NP], const int (&hi)[NP], int ms_begin, int ms_end,
-                                 ShrinkSmem<R> &sm, f32x4_t (&res)[ShrinkSmem<R>::kNB]) {
+                                 ShrinkSmem<R> &sm, f32x4_t (&res)[ShrinkSmem<R>::kNB], RM rm) {
     constexpr int NB = ShrinkSmem<R>::kNB;
     constexpr int kALoads = ShrinkSmem<R>::kALoads;
     constexpr int S = ShrinkSmem<R>::kStages;
@@ -277,7 +277,8 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP],
         rhi = max(rhi, hi[p]);
         touches[p] = t0 + 16 * wave < hi[p] && t0 + 16 * wave + 16 > lo[p];
     }
-    const bf16_t *xrow = X + (size_t)min(max(row, rlo), rhi - 1) * d_in;  // rows outside: never stored
+    // rows outside the pieces are never stored; rm gives the token row
+    const bf16_t *xrow = X + (size_t)rm(min(max(row, rlo), rhi - 1)) * d_in;
     // Every step of the loop is straight-line: a step past ms_end (padding to
     // a multiple of S) or a slice past d_in loads a clamped address and its
     // operands are zeroed, never skipped, so each group of loads stays in
@@ -449,10 +450,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // kVEarly: V is final before the launch (a separate shrink), so it is
 // requested together with Y.
 // load_v4(idx): V[idx .. idx + 3] (idx a multiple of 4).
-template <int R, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready>
+// rm(p, ok): the row of Y that segment row p updates (never stored if !ok).
+template <int R, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready,
+          typename RM>
 __device__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, float scale,
                                  ExpandSmem<R> &sm, const PieceList &pl, Gather gather, BkOf bk_of,
-                                 LoadV4 load_v4, Ready ready) {
+                                 LoadV4 load_v4, Ready ready, RM rm) {
     constexpr int K = ExpandSmem<R>::kK;
     constexpr int KS = K / 32;                                   // MFMA steps over the rank
     constexpr int kBt = ExpandSmem<R>::kBtStride;
@@ -469,13 +472,17 @@ __device__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, fl
     // and columns past d_out load a clamped address and are never stored.
     constexpr int kYPer = kTileRows * kColVecs / kBlockThreads;
     uint4 yv[kYPer];
+    int yrow[kYPer];    // row of Y behind each vector
+    uint32_t yok = 0;   // bit q: yrow[q] may be stored
     auto fetch_y = [&]() {
 #pragma unroll
         for (int q = 0; q < kYPer; ++q) {
             const int idx = tid + q * kBlockThreads;
-            const int m = min(t0 + idx / kColVecs, t1 - 1);
             const int n = n0 + (idx % kColVecs) * 8;
-            yv[q] = ld16(Y + (size_t)m * d_out + (n < d_out ? n : 0));
+            bool ok;
+            yrow[q] = rm(min(t0 + idx / kColVecs, t1 - 1), ok);
+            yok |= (uint32_t)ok << q;
+            yv[q] = ld16(Y + (size_t)yrow[q] * d_out + (n < d_out ? n : 0));
         }
     };
 
@@ -610,7 +617,8 @@ __device__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, fl
     for (int q = 0; q < kYPer; ++q) {
         const int idx = tid + q * kBlockThreads;
         const int n = n0 + (idx % kColVecs) * 8;
-        if (((touched >> q) & 1u) && n < d_out) st16(Y + (size_t)(t0 + idx / kColVecs) * d_out + n, yv[q]);
+        const int row = RM::kIndexed ? yrow[q] : t0 + idx / kColVecs;  // contiguous: a touched row is in the tile
+        if ((((touched & yok) >> q) & 1u) && n < d_out) st16(Y + (size_t)row * d_out + n, yv[q]);
     }
 }
 

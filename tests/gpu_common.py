@@ -80,3 +80,35 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def oracle_bits(orc, y: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     return orc.round_bf16(y) if dtype == torch.bfloat16 else orc.round_f32(y)
+
+
+# -- the batch in token order (gathered calls) --------------------------------
+def rows_tensor(rows, dev) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(rows, np.int32)).to(dev)
+
+
+def run_split_gather(c: DeviceCase, rows: torch.Tensor, Y=None, workspace=None):
+    V = torch.zeros((c.w.M, c.w.r), dtype=torch.float32, device=c.X.device)
+    Y = c.Y0.clone() if Y is None else Y
+    sg.sgmv_shrink_gather(V, c.X, rows, c.A_ptrs, c.seg_start, c.seg_adapter, c.w.r,
+                          workspace_buf=workspace)
+    sg.sgmv_expand_scatter(Y, V, rows, c.B_ptrs, c.seg_start, c.seg_adapter, c.w.r, c.w.alpha)
+    torch.cuda.synchronize()
+    return V, Y
+
+
+def run_fused_gather(c: DeviceCase, rows: torch.Tensor, Y=None, workspace=None):
+    Y = c.Y0.clone() if Y is None else Y
+    sg.sgmv_fused_gather(Y, c.X, rows, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, c.w.r, c.w.alpha,
+                         workspace_buf=workspace)
+    torch.cuda.synchronize()
+    return Y
+
+
+def oracle_run_gather(orc, w: wl.Workload, rows):
+    """The oracle on a batch whose X and Y are in token order: segment row p
+    is token rows[p]. Returns V (segment order) and Y (token order)."""
+    V = orc.shrink_gather(wl.storage(w.X), wl.storage(w.A_pool), w.seg_start, w.seg_adapter, rows)
+    Y = orc.expand_scatter(wl.storage(w.Y), V, wl.storage(w.B_pool), w.seg_start, w.seg_adapter, rows,
+                           w.alpha)
+    return V, Y

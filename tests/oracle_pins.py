@@ -29,6 +29,9 @@ What each pin rests on:
   conversion, and with hand-checked ties.
 * segments — the grouping of tokens by adapter is a stable sort with correct
   run starts.
+* gather_per_token — with the batch left in token order, the gathered call
+  gives every token the per-row equation with its own adapter, worked in
+  Python integers without segments; V comes back in segment order.
 """
 from __future__ import annotations
 
@@ -301,6 +304,45 @@ def pin_segments(build_segments):
     assert list(perm) == [1, 3, 0, 2, 4] and list(ss) == [0, 2, 5] and list(sa) == [0, 1]
 
 
+def pin_gather_per_token(orc, build_segments=None):
+    """The batch left in token order: tokens carry adapter ids in any order,
+    the grouping gives (perm, offsets, ids), and the gathered call with
+    rows = perm must give every token t exactly the per-row equation with its
+    own adapter, y_t += (alpha/r) x_t A_k(t) B_k(t) (Punica guide, "The
+    Heterogeneous Batching Bottleneck"), worked in Python integers with no
+    segments at all. V comes back in segment order: V[p] belongs to token
+    perm[p]."""
+    import oracle as oracle_pkg
+    build_segments = build_segments or oracle_pkg.build_segments
+    rng = np.random.Generator(np.random.PCG64(22))
+    for _ in range(12):
+        M = int(rng.integers(1, 13))
+        P = int(rng.integers(1, 5))
+        r = int(rng.choice([8, 16]))
+        d_in, d_out = 8 * int(rng.integers(1, 4)), 8 * int(rng.integers(1, 4))
+        ids = rng.integers(0, P, size=M).astype(np.int32)
+        perm, ss, sa = build_segments(ids)
+        w = wl.Workload("gather", M, d_in, d_out, r, 2.0 * r, torch.bfloat16, P, ss, sa)
+        wl.integer_case(rng, w)
+        X = w.X.to(torch.int64).tolist()
+        A = w.A_pool.to(torch.int64).tolist()
+        B = w.B_pool.to(torch.int64).tolist()
+        Y = w.Y.to(torch.int64).tolist()
+        Vt = []
+        for t in range(M):
+            k = int(ids[t])
+            v = [sum(X[t][i] * A[k][j][i] for i in range(d_in)) for j in range(r)]
+            Vt.append(v)
+            for n in range(d_out):
+                Y[t][n] += 2 * sum(v[j] * B[k][j][n] for j in range(r))
+        args = (wl.storage(w.A_pool), wl.storage(w.B_pool), ss, sa)
+        got = orc.sgmv_gather(wl.storage(w.Y), wl.storage(w.X), *args, perm, w.alpha)
+        assert np.array_equal(got, np.array(Y, dtype=np.float64).reshape(M, d_out))
+        V = orc.shrink_gather(wl.storage(w.X), wl.storage(w.A_pool), ss, sa, perm)
+        want_v = np.array([Vt[int(t)] for t in perm], dtype=np.float64).reshape(M, r)
+        assert np.array_equal(V, want_v)
+
+
 ALL_PINS = [pin_dense_single_adapter, pin_dense_mask, pin_integer_bruteforce, pin_handworked,
             pin_zero_adapter, pin_linearity, pin_permutation, pin_signature, pin_scale,
-            pin_bf16_rounding]
+            pin_bf16_rounding, pin_gather_per_token]

@@ -41,7 +41,7 @@ def test_status_strings():
 # Distinct 256-byte aligned fake device addresses. They are never
 # dereferenced: each call below fails its argument checks (or is a no-op)
 # before anything is enqueued.
-P1, P2, P3, P4, P5, P6 = (0x100000 * (i + 1) for i in range(6))
+P1, P2, P3, P4, P5, P6, P7 = (0x100000 * (i + 1) for i in range(7))
 
 
 def shrink(V=P1, X=P2, A=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, r=16, dt=1, ws=0x800000,
@@ -58,25 +58,52 @@ def fused(Y=P1, X=P2, A=P3, B=P6, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, d_out=64
     return sg.lib.sgmv_fused(Y, X, A, B, P, ss, sa, N, M, d_in, d_out, r, 32.0, dt, ws, wsb, None)
 
 
-@pytest.mark.parametrize("call", [shrink, expand, fused])
+def shrink_gather(V=P1, X=P2, rows=P7, A=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, r=16, dt=1,
+                  ws=0x800000, wsb=1 << 20):
+    return sg.lib.sgmv_shrink_gather(V, X, rows, A, P, ss, sa, N, M, d_in, r, dt, ws, wsb, None)
+
+
+def expand_scatter(Y=P1, V=P2, rows=P7, B=P3, P=4, ss=P4, sa=P5, N=2, M=4, d_out=64, r=16, alpha=32.0,
+                   dt=1):
+    return sg.lib.sgmv_expand_scatter(Y, V, rows, B, P, ss, sa, N, M, d_out, r, alpha, dt, None)
+
+
+def fused_gather(Y=P1, X=P2, rows=P7, A=P3, B=P6, P=4, ss=P4, sa=P5, N=2, M=4, d_in=64, d_out=64, r=16,
+                 dt=1, ws=0x800000, wsb=1 << 20):
+    return sg.lib.sgmv_fused_gather(Y, X, rows, A, B, P, ss, sa, N, M, d_in, d_out, r, 32.0, dt, ws, wsb,
+                                    None)
+
+
+ALL_CALLS = [shrink, expand, fused, shrink_gather, expand_scatter, fused_gather]
+GATHERED = [shrink_gather, expand_scatter, fused_gather]
+
+
+@pytest.mark.parametrize("call", ALL_CALLS, ids=lambda f: f.__name__)
 def test_argument_errors(call):
     assert call(r=12) == -3 and call(r=0) == -3 and call(r=128) == -3
     assert call(dt=2) == -4 and call(dt=-1) == -4
     assert call(M=-1) == -2 and call(N=-1) == -2 and call(P=-1) == -2
-    dim = "d_in" if call is not expand else "d_out"
+    dim = "d_out" if call in (expand, expand_scatter) else "d_in"
     assert call(**{dim: 12}) == -2 and call(**{dim: 0}) == -2
-    first = "V" if call is shrink else "Y"
+    first = "V" if call in (shrink, shrink_gather) else "Y"
     assert call(**{first: None}) == -1
     assert call(ss=None) == -1 and call(sa=None) == -1
     assert call(**{first: P1 + 8}) == -5
 
 
-@pytest.mark.parametrize("call", [shrink, expand, fused])
+@pytest.mark.parametrize("call", ALL_CALLS, ids=lambda f: f.__name__)
 def test_empty_is_noop(call):
     # nothing to do: OK without touching any pointer, even NULL ones
-    first = "V" if call is shrink else "Y"
+    first = "V" if call in (shrink, shrink_gather) else "Y"
     assert call(M=0, **{first: None}) == 0
     assert call(N=0, ss=None, sa=None) == 0
+
+
+@pytest.mark.parametrize("call", GATHERED, ids=lambda f: f.__name__)
+def test_gathered_calls_need_rows(call):
+    assert call(rows=None) == -1
+    assert call(M=0, rows=None) == 0
+    assert call(rows=None, r=12) == -3   # the same order of checks as the contiguous call
 
 
 def test_fused_workspace_checks():

@@ -8,6 +8,7 @@ modified."""
 import tempfile
 from pathlib import Path
 
+import numpy as np
 import pytest
 
 import oracle as oracle_pkg
@@ -66,3 +67,37 @@ def test_mutant_is_caught(name, old, new, which):
             except (AssertionError, ValueError):
                 failed.append(pin.__name__)
         assert failed, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the oracle's gather/scatter layer (Python): each must
+# fail the per-token pin.
+def _inverse(rows):
+    return np.argsort(np.asarray(rows, np.int64))
+
+
+class _GatherInverse(oracle_pkg.Oracle):
+    def shrink_gather(self, X, A_pool, seg_start, seg_adapter, rows):
+        return super().shrink_gather(X, A_pool, seg_start, seg_adapter, _inverse(rows))
+
+
+class _NoGather(oracle_pkg.Oracle):
+    def shrink_gather(self, X, A_pool, seg_start, seg_adapter, rows):
+        return self.shrink(X, A_pool, seg_start, seg_adapter)
+
+
+class _ScatterInverse(oracle_pkg.Oracle):
+    def expand_scatter(self, Y_in, V, B_pool, seg_start, seg_adapter, rows, alpha):
+        return super().expand_scatter(Y_in, V, B_pool, seg_start, seg_adapter, _inverse(rows), alpha)
+
+
+class _NoScatter(oracle_pkg.Oracle):
+    def expand_scatter(self, Y_in, V, B_pool, seg_start, seg_adapter, rows, alpha):
+        return self.expand(Y_in, V, B_pool, seg_start, seg_adapter, alpha)
+
+
+@pytest.mark.parametrize("cls", [_GatherInverse, _NoGather, _ScatterInverse, _NoScatter],
+                         ids=lambda c: c.__name__.strip("_"))
+def test_gather_mutant_is_caught(cls):
+    orc = cls()
+    with pytest.raises(AssertionError):
+        pins.pin_gather_per_token(orc)

@@ -9,6 +9,13 @@ over one batch. To keep the 256 MB Infinity Cache from serving the weights,
 the steps rotate over R replicas of the pools and activations (each its own
 HBM region), so a replica's bytes are cold when it comes round again.
 
+Paths: fused (one launch) and split (shrink, then expand) take the batch in
+segment order; fused_gather and split_gather take it in token order with a
+row index (for decode_skewed the grouping's own permutation, for the other
+workloads a seeded shuffle); fused_permute is the comparison for those: torch
+row gathers of X and Y into segment order around the contiguous fused call,
+and a torch scatter of Y back.
+
 Prints ONE JSON line: value = algorithmic HBM GB/s (X read once, each
 segment's adapter read once, Y read and written once) over the timed steps,
 plus a roofline object for the dominant kernel and the CPU oracle's rate on
@@ -49,7 +56,11 @@ def profiled_traffic(workload, path, kernel):
     no summary or the kernel sources have changed since it was taken."""
     import re
     from pathlib import Path
-    name = ("fused" if path == "fused" else "shrink_expand") + f"_{workload}.md"
+    prefix = {"fused": "fused", "split": "shrink_expand", "fused_gather": "fused_gather",
+              "split_gather": "shrink_expand_gather"}.get(path)
+    if prefix is None:
+        return None
+    name = f"{prefix}_{workload}.md"
     f = Path(ROOT) / "profiles" / name
     if not f.exists():
         return None
@@ -70,7 +81,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_distinct",
                    choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b"])
-    p.add_argument("--path", default="fused", choices=["split", "fused"])
+    p.add_argument("--path", default="fused",
+                   choices=["split", "fused", "split_gather", "fused_gather", "fused_permute"])
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,6 +106,21 @@ class Replica:
         self.seg_start = torch.from_numpy(np.ascontiguousarray(w.seg_start, np.int32)).to(dev)
         self.seg_adapter = torch.from_numpy(np.ascontiguousarray(w.seg_adapter, np.int32)).to(dev)
         self.V = torch.zeros((w.M, w.r), dtype=torch.float32, device=dev)
+        rows = token_rows(w)
+        self.rows = torch.from_numpy(rows).to(dev)                    # int32, for the gathered calls
+        self.rows64 = torch.from_numpy(rows.astype(np.int64)).to(dev)  # for torch's row permutes
+        self.Xs = torch.empty_like(X)   # segment-order copies (fused_permute)
+        self.Ys = torch.empty_like(Y)
+
+
+def token_rows(w):
+    """Token row of each segment row: decode_skewed keeps its draw's arrival
+    order (the grouping's permutation); other workloads get a seeded
+    shuffle."""
+    if w.token_adapter is not None:
+        order = np.argsort(np.asarray(w.token_adapter, np.int64), kind="stable")
+        return order.astype(np.int32)
+    return np.random.Generator(np.random.PCG64(90)).permutation(w.M).astype(np.int32)
 
 
 def make_workloads(name):
@@ -131,15 +158,30 @@ def build_replicas(ws, dev, R):
 
 
 def step(group, path, ws=None):
+    import torch
     import segmented_gather_gemm_sgmv_amd as sg
     for rp in group:
         w = rp.w
         if path == "fused":
             sg.sgmv_fused(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
                           workspace_buf=ws)
-        else:
+        elif path == "split":
             sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r, workspace_buf=ws)
             sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
+        elif path == "fused_gather":
+            sg.sgmv_fused_gather(rp.Y, rp.X, rp.rows, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter,
+                                 w.r, w.alpha, workspace_buf=ws)
+        elif path == "split_gather":
+            sg.sgmv_shrink_gather(rp.V, rp.X, rp.rows, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r,
+                                  workspace_buf=ws)
+            sg.sgmv_expand_scatter(rp.Y, rp.V, rp.rows, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r,
+                                   w.alpha)
+        else:  # fused_permute: the caller moves rows into segment order and back
+            torch.index_select(rp.X, 0, rp.rows64, out=rp.Xs)
+            torch.index_select(rp.Y, 0, rp.rows64, out=rp.Ys)
+            sg.sgmv_fused(rp.Ys, rp.Xs, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha,
+                          workspace_buf=ws)
+            rp.Y.index_copy_(0, rp.rows64, rp.Ys)
 
 
 def capture(reps, path, first, count, ws):
@@ -153,8 +195,13 @@ def capture(reps, path, first, count, ws):
     return g
 
 
+KERNELS = {"fused": ["fused"], "split": ["shrink", "expand"], "fused_gather": ["fused_gather"],
+           "split_gather": ["shrink_gather", "expand_scatter"], "fused_permute": ["fused"]}
+
+
 def kernel_bytes(w, path):
-    """Algorithmic bytes per launch of each kernel of the path."""
+    """Algorithmic bytes per launch of each kernel of the path (the row
+    index, like the segment metadata, is a few KB and not counted)."""
     e = 4 if str(w.dtype).endswith("float32") else 2
     N = w.num_segments
     x = e * w.M * w.d_in
@@ -162,9 +209,10 @@ def kernel_bytes(w, path):
     b = e * N * w.r * w.d_out
     y = 2 * e * w.M * w.d_out
     v = 4 * w.M * w.r
-    if path == "fused":
-        return {"fused": x + a + b + y}
-    return {"shrink": x + a + v, "expand": b + y + v}
+    if path in ("fused", "fused_gather", "fused_permute"):
+        return {KERNELS[path][0]: x + a + b + y}
+    names = KERNELS[path]
+    return {names[0]: x + a + v, names[1]: b + y + v}
 
 
 def launch_kernel(rp, name, ws=None):
@@ -175,8 +223,16 @@ def launch_kernel(rp, name, ws=None):
                       workspace_buf=ws)
     elif name == "shrink":
         sg.sgmv_shrink(rp.V, rp.X, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r, workspace_buf=ws)
-    else:
+    elif name == "expand":
         sg.sgmv_expand(rp.Y, rp.V, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
+    elif name == "fused_gather":
+        sg.sgmv_fused_gather(rp.Y, rp.X, rp.rows, rp.A_ptrs, rp.B_ptrs, rp.seg_start, rp.seg_adapter,
+                             w.r, w.alpha, workspace_buf=ws)
+    elif name == "shrink_gather":
+        sg.sgmv_shrink_gather(rp.V, rp.X, rp.rows, rp.A_ptrs, rp.seg_start, rp.seg_adapter, w.r,
+                              workspace_buf=ws)
+    else:
+        sg.sgmv_expand_scatter(rp.Y, rp.V, rp.rows, rp.B_ptrs, rp.seg_start, rp.seg_adapter, w.r, w.alpha)
 
 
 def time_kernels(reps, path, steps, wsbuf):
@@ -185,7 +241,7 @@ def time_kernels(reps, path, steps, wsbuf):
     until `steps` launches were timed, bracketed by HIP events recorded on the
     replay stream."""
     import torch
-    names = ["fused"] if path == "fused" else ["shrink", "expand"]
+    names = KERNELS[path]
     R = len(reps)
     out = {}
     for name in names:
@@ -327,7 +383,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w0.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "path": "shrink+expand" if args.path == "split" else "fused",
+        "config": {"workload": args.workload,
+                   "path": {"split": "shrink+expand", "split_gather": "shrink_gather+expand_scatter"}.get(
+                       args.path, args.path),
                    "d_in": w0.d_in, "d_out": w0.d_out, "r": w0.r, "alpha": w0.alpha, "tokens": w0.M,
                    "segments": w0.num_segments, "pool": w0.num_adapters, "projections": len(ws),
                    "replicas": R, "algorithmic_bytes_per_step": nbytes},

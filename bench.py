@@ -14,7 +14,8 @@ segment order; fused_gather and split_gather take it in token order with a
 row index (for decode_skewed the grouping's own permutation, for the other
 workloads a seeded shuffle); fused_permute is the comparison for those: torch
 row gathers of X and Y into segment order around the contiguous fused call,
-and a torch scatter of Y back.
+and a torch scatter of Y back. fused_layer runs all projections of a step
+(the 70B slice's seven) in one launch.
 
 Prints ONE JSON line: value = algorithmic HBM GB/s (X read once, each
 segment's adapter read once, Y read and written once) over the timed steps,
@@ -57,7 +58,7 @@ def profiled_traffic(workload, path, kernel):
     import re
     from pathlib import Path
     prefix = {"fused": "fused", "split": "shrink_expand", "fused_gather": "fused_gather",
-              "split_gather": "shrink_expand_gather"}.get(path)
+              "split_gather": "shrink_expand_gather", "fused_layer": "fused_layer"}.get(path)
     if prefix is None:
         return None
     name = f"{prefix}_{workload}.md"
@@ -80,9 +81,9 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_distinct",
-                   choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b"])
+                   choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b", "layer7b"])
     p.add_argument("--path", default="fused",
-                   choices=["split", "fused", "split_gather", "fused_gather", "fused_permute"])
+                   choices=["split", "fused", "split_gather", "fused_gather", "fused_permute", "fused_layer"])
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,6 +135,8 @@ def make_workloads(name):
         return [wl.decode_skewed(sg.sgmv_build_segments)]
     if name == "prefill":
         return [wl.prefill()]
+    if name == "layer7b":
+        return wl.layer7b()
     return wl.slice70b()
 
 
@@ -157,9 +160,19 @@ def build_replicas(ws, dev, R):
     return reps
 
 
+def layer_call(group, ws=None):
+    import segmented_gather_gemm_sgmv_amd as sg
+    rp0 = group[0]
+    sg.sgmv_fused_layer([(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs) for rp in group], rp0.seg_start, rp0.seg_adapter,
+                        rp0.w.r, rp0.w.alpha, workspace_buf=ws)
+
+
 def step(group, path, ws=None):
     import torch
     import segmented_gather_gemm_sgmv_amd as sg
+    if path == "fused_layer":
+        layer_call(group, ws)
+        return
     for rp in group:
         w = rp.w
         if path == "fused":
@@ -196,7 +209,8 @@ def capture(reps, path, first, count, ws):
 
 
 KERNELS = {"fused": ["fused"], "split": ["shrink", "expand"], "fused_gather": ["fused_gather"],
-           "split_gather": ["shrink_gather", "expand_scatter"], "fused_permute": ["fused"]}
+           "split_gather": ["shrink_gather", "expand_scatter"], "fused_permute": ["fused"],
+           "fused_layer": ["fused_layer"]}
 
 
 def kernel_bytes(w, path):
@@ -209,7 +223,7 @@ def kernel_bytes(w, path):
     b = e * N * w.r * w.d_out
     y = 2 * e * w.M * w.d_out
     v = 4 * w.M * w.r
-    if path in ("fused", "fused_gather", "fused_permute"):
+    if path in ("fused", "fused_gather", "fused_permute", "fused_layer"):
         return {KERNELS[path][0]: x + a + b + y}
     names = KERNELS[path]
     return {names[0]: x + a + v, names[1]: b + y + v}
@@ -248,6 +262,9 @@ def time_kernels(reps, path, steps, wsbuf):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for group in reps:
+                if name == "fused_layer":
+                    layer_call(group, wsbuf)
+                    continue
                 for rp in group:
                     launch_kernel(rp, name, wsbuf)
         g.replay()
@@ -260,7 +277,7 @@ def time_kernels(reps, path, steps, wsbuf):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        launches = n_replays * sum(len(gr) for gr in reps)
+        launches = n_replays * (len(reps) if name == "fused_layer" else sum(len(gr) for gr in reps))
         out[name] = a.elapsed_time(b) * 1e3 / launches   # microseconds per launch
         del g
     return out
@@ -321,6 +338,9 @@ def main():
     # one zero-filled workspace serves every fused call (they run in order on
     # one stream and each returns the control words to zero)
     need = max(sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype) for w in ws)
+    if args.path == "fused_layer":
+        need = sg.sgmv_layer_workspace_bytes([(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs) for rp in reps[0]],
+                                             ws[0].num_segments, ws[0].M, ws[0].r, ws[0].dtype)
     wsbuf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
     for i in range(args.warmup):
@@ -347,7 +367,9 @@ def main():
     # per-kernel durations, for the roofline
     kus = time_kernels(reps, args.path, args.steps, wsbuf)
     per_kernel = kernel_bytes(ws[0], args.path)
-    if len(ws) > 1:  # several projections: average bytes per launch, as kus averages time
+    if args.path == "fused_layer":  # one launch covers every projection
+        per_kernel = {"fused_layer": sum(w.algorithmic_bytes() for w in ws)}
+    elif len(ws) > 1:  # several projections: average bytes per launch, as kus averages time
         for w in ws[1:]:
             for n, b in kernel_bytes(w, args.path).items():
                 per_kernel[n] += b

@@ -170,6 +170,54 @@ int sgmv_fused_gather(void *Y, const void *X, const int32_t *rows, const uint64_
                       int32_t d_out, int32_t r, float alpha, int32_t dtype, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/*
+ * Layer-batched fused call: every projection of one batch in one launch
+ * (Punica guide, "Mathematical Modeling", equation 2: the execution latency
+ * of a layer counts its launches, one per adapter matrix; here one per layer,
+ * whatever the number of projections).
+ *
+ * For every projection q < num_projections, with p = projections[q]:
+ *     p.Y[m, :] += (alpha / r) * p.X[m, :] . A_k . B_k
+ * where A_k and B_k come from p's own pools (p.A_ptrs, p.B_ptrs, each of
+ * p.num_adapters entries) and k is the adapter of m's segment. All
+ * projections share the batch: M rows, the segments (seg_start,
+ * seg_adapter), r, alpha and dtype; each has its own d_in and d_out, and X
+ * and Y of the layouts above (p.X: M x p.d_in, p.Y: M x p.d_out). The
+ * result is that of one sgmv_fused call per projection.
+ *
+ * rows         NULL: X and Y in segment order. Otherwise the token-order
+ *              index of the gathered calls above, shared by every projection.
+ * projections  host array of num_projections descriptors, read during the
+ *              call only (the library keeps no pointer to it).
+ * num_projections  0 .. SGMV_MAX_PROJECTIONS (0 is a no-op).
+ * workspace    at least sgmv_layer_workspace_bytes(...) bytes, 256-byte
+ *              aligned, zero-filled before first use; every call leaves it
+ *              zero again (as for sgmv_fused).
+ * The Y buffers of different projections must not overlap. Errors and
+ * device-side defences as for sgmv_fused, checked for every projection;
+ * num_projections outside [0, SGMV_MAX_PROJECTIONS] is SGMV_ERR_SHAPE.
+ */
+#define SGMV_MAX_PROJECTIONS 8
+
+typedef struct sgmv_projection {
+    void *Y;
+    const void *X;
+    const uint64_t *A_ptrs;
+    const uint64_t *B_ptrs;
+    int32_t num_adapters;
+    int32_t d_in;
+    int32_t d_out;
+} sgmv_projection;
+
+int sgmv_fused_layer(const sgmv_projection *projections, int32_t num_projections, const int32_t *rows,
+                     const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments, int32_t M,
+                     int32_t r, float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Workspace bytes sgmv_fused_layer needs (0 on invalid arguments). */
+size_t sgmv_layer_workspace_bytes(const sgmv_projection *projections, int32_t num_projections,
+                                  int32_t num_segments, int32_t M, int32_t r, int32_t dtype);
+
 /* Bytes of workspace sgmv_shrink and sgmv_fused need for these sizes; one
  * buffer of this size serves both (0 on invalid sizes, or when neither needs
  * any). The gathered forms need the same. */

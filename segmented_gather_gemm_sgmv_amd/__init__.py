@@ -42,6 +42,9 @@ EXPORTS = {
                                            _i32, _vp]),
     "sgmv_fused_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _i32, _vp, _sz, _vp]),
+    "sgmv_fused_layer": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                        _vp]),
+    "sgmv_layer_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
     "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
@@ -252,6 +255,62 @@ def sgmv_fused_gather(Y: torch.Tensor, X: torch.Tensor, rows: torch.Tensor, A_pt
     return Y
 
 
+SGMV_MAX_PROJECTIONS = 8
+
+
+class SgmvProjection(ctypes.Structure):
+    """``sgmv_projection`` of include/sgmv.h: one projection of a layer call."""
+    _fields_ = [("Y", ctypes.c_void_p), ("X", ctypes.c_void_p), ("A_ptrs", ctypes.c_void_p),
+                ("B_ptrs", ctypes.c_void_p), ("num_adapters", ctypes.c_int32), ("d_in", ctypes.c_int32),
+                ("d_out", ctypes.c_int32)]
+
+
+def _projection_array(projections, check=True):
+    """(Y, X, A_ptrs, B_ptrs) tuples -> a ctypes array of SgmvProjection."""
+    arr = (SgmvProjection * max(1, len(projections)))()
+    for q, (Y, X, A_ptrs, B_ptrs) in enumerate(projections):
+        if check:
+            if X.shape[0] != Y.shape[0]:
+                raise ValueError(f"projection {q}: X and Y must have the same number of rows")
+            if A_ptrs.numel() != B_ptrs.numel():
+                raise ValueError(f"projection {q}: A_ptrs and B_ptrs must have one entry per adapter")
+        arr[q] = SgmvProjection(_dev(Y, "Y", dim=2), _dev(X, "X", dim=2),
+                                _dev(A_ptrs, "A_ptrs", torch.int64, 1), _dev(B_ptrs, "B_ptrs", torch.int64, 1),
+                                A_ptrs.numel(), X.shape[1], Y.shape[1])
+    return arr
+
+
+def sgmv_layer_workspace_bytes(projections, num_segments: int, M: int, r: int, dtype: torch.dtype) -> int:
+    arr = _projection_array(projections)
+    return int(lib.sgmv_layer_workspace_bytes(arr, len(projections), num_segments, M, r, _DTYPES[dtype]))
+
+
+def sgmv_fused_layer(projections, seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int, alpha: float,
+                     rows: Optional[torch.Tensor] = None, workspace_buf: Optional[torch.Tensor] = None,
+                     stream=None):
+    """Every projection (Y, X, A_ptrs, B_ptrs) of one batch in one launch:
+    Y += (alpha / r) * X . A_k . B_k per projection (in place). ``rows``: None
+    for a batch in segment order, else the token-order index."""
+    if not projections:
+        return
+    Y0, X0 = projections[0][0], projections[0][1]
+    M = X0.shape[0]
+    for Y, X, _, _ in projections:
+        if X.shape[0] != M or Y.shape[0] != M:
+            raise ValueError("every projection must have the batch's M rows")
+        if X.dtype != X0.dtype or Y.dtype != X0.dtype:
+            raise TypeError("every projection must share one dtype")
+    arr = _projection_array(projections)
+    need = int(lib.sgmv_layer_workspace_bytes(arr, len(projections), seg_adapter.numel(), M, r,
+                                              _dtype_code(X0)))
+    ws, ws_bytes = _workspace_args(workspace_buf, need, X0, stream)
+    rows_p = None if rows is None else _rows_arg(rows, M)
+    st = lib.sgmv_fused_layer(arr, len(projections), rows_p, _dev(seg_start, "seg_start", torch.int32, 1),
+                              _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(), M, r,
+                              float(alpha), _dtype_code(X0), ws, ws_bytes, _stream(X0, stream))
+    _check("sgmv_fused_layer", st)
+
+
 def sgmv_build_segments(token_adapter) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Host: group tokens by adapter. Returns (perm, seg_start, seg_adapter)."""
     ids = np.ascontiguousarray(np.asarray(token_adapter, dtype=np.int32))
@@ -288,6 +347,7 @@ def sgmv_version() -> int:
 
 
 __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sgmv_expand_scatter",
-           "sgmv_fused_gather", "sgmv_workspace_bytes", "sgmv_build_segments",
+           "sgmv_fused_gather", "sgmv_fused_layer", "sgmv_layer_workspace_bytes", "SgmvProjection",
+           "SGMV_MAX_PROJECTIONS", "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16"]

@@ -184,6 +184,72 @@ int sgmv_fused_gather(void *Y, const void *X, const int32_t *rows, const uint64_
                       num_segments, M, d_in, d_out, r, alpha, dtype, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Copies and checks the host descriptors; SGMV_OK and *count = 0 when there is
+// nothing to do.
+int layer_inputs(const sgmv_projection *projections, int32_t num_projections, int32_t num_segments, int32_t M,
+                 int32_t r, int32_t dtype, sgmv::LayerProjIn *out) {
+    if (num_projections < 0 || num_projections > SGMV_MAX_PROJECTIONS) return SGMV_ERR_SHAPE;
+    if (num_projections > 0 && !projections) return SGMV_ERR_NULL;
+    for (int32_t q = 0; q < num_projections; ++q) {
+        const sgmv_projection &p = projections[q];
+        int st = check_common(p.num_adapters, num_segments, M, r, dtype);
+        if (st != SGMV_OK) return st;
+        if (!valid_dim(p.d_in) || !valid_dim(p.d_out) || (int64_t)M * p.d_in > kMaxElems ||
+            (int64_t)M * p.d_out > kMaxElems)
+            return SGMV_ERR_SHAPE;
+        out[q] = sgmv::LayerProjIn{p.Y, p.X, p.A_ptrs, p.B_ptrs, p.num_adapters, p.d_in, p.d_out};
+    }
+    return SGMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sgmv_layer_workspace_bytes(const sgmv_projection *projections, int32_t num_projections,
+                                  int32_t num_segments, int32_t M, int32_t r, int32_t dtype) {
+    sgmv::LayerProjIn in[sgmv::kMaxProjections];
+    if (layer_inputs(projections, num_projections, num_segments, M, r, dtype, in) != SGMV_OK) return 0;
+    return sgmv::layer_workspace_total(in, num_projections, num_segments, M, r, dtype);
+}
+
+int sgmv_fused_layer(const sgmv_projection *projections, int32_t num_projections, const int32_t *rows,
+                     const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments, int32_t M,
+                     int32_t r, float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (!valid_dtype(dtype)) return SGMV_ERR_DTYPE;
+    if (!valid_rank(r)) return SGMV_ERR_RANK;
+    sgmv::LayerCall a{};
+    int st = layer_inputs(projections, num_projections, num_segments, M, r, dtype, a.p);
+    if (st != SGMV_OK) return st;
+    if (M < 0 || num_segments < 0) return SGMV_ERR_SHAPE;
+    if (num_projections == 0 || M == 0 || num_segments == 0) return SGMV_OK;
+    if (!seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    for (int32_t q = 0; q < num_projections; ++q) {
+        const sgmv::LayerProjIn &p = a.p[q];
+        if (!p.Y || !p.X || !p.A_ptrs || !p.B_ptrs) return SGMV_ERR_NULL;
+        if (!aligned16(p.Y) || !aligned16(p.X)) return SGMV_ERR_ALIGN;
+    }
+    st = check_workspace(workspace, workspace_bytes,
+                         sgmv::layer_workspace_total(a.p, num_projections, num_segments, M, r, dtype));
+    if (st != SGMV_OK) return st;
+    a.num_projections = num_projections;
+    a.seg_start = seg_start;
+    a.seg_adapter = seg_adapter;
+    a.num_segments = num_segments;
+    a.M = M;
+    a.r = r;
+    a.dtype = dtype;
+    a.scale = alpha / (float)r;
+    a.workspace = workspace;
+    a.rows = rows;
+    return hip_status(sgmv::launch_fused_layer(a, static_cast<hipStream_t>(stream)));
+}
+
 int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
                         int32_t *seg_start, int32_t *seg_adapter, int32_t *num_segments) {
     if (M < 0) return SGMV_ERR_SHAPE;

@@ -659,14 +659,18 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 // workgroups still run.
 constexpr int kFusedRB = 4;
 
+// One work item of the fused launch: `item` is its id inside the launch's
+// item layout (the workgroup id for a launch of one projection, the offset
+// inside the projection's region for a layer-batched launch; congruent to
+// the workgroup id modulo 8 either way, so the XCD placement is the same).
 template <typename T, int R, bool kGather>
-__global__ __launch_bounds__(kBlock) void fused_kernel(
+__device__ __forceinline__ void fused_item(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
     int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials, RowMap<kGather> rm) {
+    float *Vpairs, float *partials, RowMap<kGather> rm, const int item) {
     // each segment and each 64-row tile owns one cache line of counters. A
     // segment's word 1 counts expand departures (the vector path hands V over
     // as flagged pairs, Vpairs). A tile's word 0 counts the shrink parts
@@ -681,7 +685,6 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
-    const int item = blockIdx.x;
     const int a0 = round_up_xcds(num_segments) * groups;  // vector shrink items
     const int a1 = a0 + num_tiles * ks;                   // MFMA shrink items (64 rows x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
@@ -747,7 +750,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
                 publish(&tile_arrive[t * kCounterStride]);
             return;
         }
-        const int e = xcd_local_item(a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
+        const int e = xcd_local_item(item, a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
         if (e < 0) return;
         const int t = e / ntiles_m;
         const int t0 = t * kTileRows;
@@ -788,6 +791,43 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
             reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
         }
     }
+}
+
+template <typename T, int R, bool kGather>
+__global__ __launch_bounds__(kBlock) void fused_kernel(
+    T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
+    const uint64_t *__restrict__ B_ptrs, int num_adapters,
+    const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
+    int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
+    int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
+    float *Vpairs, float *partials, RowMap<kGather> rm) {
+    fused_item<T, R, kGather>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
+                              d_in, d_out, ntiles_g, ntiles_m, num_tiles, ks, scale, long_batch,
+                              seg_counters, tile_counters, Vws, Vpairs, partials, rm, (int)blockIdx.x);
+}
+
+// Layer-batched fused launch (the launch accounting of the Punica guide's
+// "Mathematical Modeling", extended from one layer's A and B launches to all
+// of its projections): every projection of one batch in one launch. Each
+// projection keeps the item layout of its own fused launch, in a region of
+// workgroup ids starting at a multiple of 8; regions follow one another in
+// projection order. Inside a region every wait is on lower ids of the same
+// region (or on the sibling parts of a split shrink tile), so the argument
+// that a fused launch's waits end carries over unchanged.
+template <typename T, int R, bool kGather>
+__global__ __launch_bounds__(kBlock) void fused_layer_kernel(
+    LayerArgs L, const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
+    int num_segments, int M, float scale, int long_batch, RowMap<kGather> rm) {
+    const int b = blockIdx.x;
+    int p = 0;
+    for (int q = 1; q < L.num_projections; ++q) p = b >= L.p[q].base ? q : p;
+    const LayerProj &d = L.p[p];
+    const int item = b - d.base;
+    if (item >= d.items) return;  // padding up to the next region
+    fused_item<T, R, kGather>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
+                              d.B_ptrs, d.num_adapters, seg_start, seg_adapter, num_segments, M, d.d_in,
+                              d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.ks, scale, long_batch,
+                              d.seg_counters, d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, item);
 }
 
 // ----------------------------------------------------------------------------
@@ -878,6 +918,51 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     return a.rows ? launch_fused_g<T, R, true>(a, st) : launch_fused_g<T, R, false>(a, st);
 }
 
+template <typename T, int R, bool kGather>
+static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
+    LayerArgs L{};
+    L.num_projections = a.num_projections;
+    char *ws = static_cast<char *>(a.workspace);
+    size_t ws_off = 0;
+    int base = 0;
+    for (int q = 0; q < a.num_projections; ++q) {
+        const LayerProjIn &in = a.p[q];
+        const FusedLayout FL = fused_layout(a.num_segments, a.M, in.d_in, a.r, a.dtype);
+        LayerProj &d = L.p[q];
+        d.Y = in.Y;
+        d.X = in.X;
+        d.A_ptrs = in.A_ptrs;
+        d.B_ptrs = in.B_ptrs;
+        d.num_adapters = in.num_adapters;
+        d.d_in = in.d_in;
+        d.d_out = in.d_out;
+        d.ntiles_g = gemv_col_tiles<T>(in.d_out);
+        d.ntiles_m = FL.tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+        d.num_tiles = FL.tiles;
+        d.ks = FL.ks;
+        char *w = ws + ws_off;
+        d.seg_counters = reinterpret_cast<uint32_t *>(w + FL.seg_counters);
+        d.tile_counters = reinterpret_cast<uint32_t *>(w + FL.tile_counters);
+        d.Vws = reinterpret_cast<float *>(w + FL.v);
+        d.Vpairs = reinterpret_cast<float *>(w + FL.vpairs);
+        d.partials = reinterpret_cast<float *>(w + FL.partials);
+        d.items = round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + FL.tiles * FL.ks +
+                  a.num_segments * d.ntiles_g + round_up_xcds(FL.tiles * d.ntiles_m);
+        d.base = base;
+        base += round_up_xcds(d.items);
+        ws_off += align256(FL.total);
+    }
+    hipLaunchKernelGGL((fused_layer_kernel<T, R, kGather>), dim3((unsigned)base), dim3(kBlock), 0, st, L,
+                       a.seg_start, a.seg_adapter, a.num_segments, a.M, a.scale,
+                       (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), RowMap<kGather>{a.rows, a.M});
+    return hipGetLastError();
+}
+
+template <typename T, int R>
+static hipError_t launch_fused_layer_t(const LayerCall &a, hipStream_t st) {
+    return a.rows ? launch_fused_layer_g<T, R, true>(a, st) : launch_fused_layer_g<T, R, false>(a, st);
+}
+
 #define SGMV_RANK_SWITCH(FN, T, args, st)           \
     switch ((args).r) {                             \
         case 8: return FN<T, 8>((args), (st));      \
@@ -900,6 +985,11 @@ hipError_t launch_expand(const ExpandArgs &a, hipStream_t st) {
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_t, float, a, st)
     SGMV_RANK_SWITCH(launch_fused_t, bf16_t, a, st)
+}
+
+hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
+    if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_layer_t, float, a, st)
+    SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_t, a, st)
 }
 
 }  // namespace sgmv

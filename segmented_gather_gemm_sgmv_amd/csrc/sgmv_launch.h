@@ -119,8 +119,62 @@ inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dt
     return L;
 }
 
+// Layer-batched fused launch: up to kMaxProjections projections of one batch
+// (shared rows, segments, rank, scale and dtype), each with its own X, Y,
+// pools and d_in / d_out, in one launch. The descriptors travel in the
+// kernel arguments.
+constexpr int kMaxProjections = 8;
+
+struct LayerProj {
+    void *Y;
+    const void *X;
+    const uint64_t *A_ptrs;
+    const uint64_t *B_ptrs;
+    uint32_t *seg_counters, *tile_counters;
+    float *Vws, *Vpairs, *partials;
+    int num_adapters, d_in, d_out;
+    int ntiles_g, ntiles_m, num_tiles, ks;
+    int base;   // first workgroup id of the projection's region (a multiple of 8)
+    int items;  // items of its own fused launch
+};
+
+struct LayerArgs {
+    LayerProj p[kMaxProjections];
+    int num_projections;
+};
+
+struct LayerProjIn {
+    void *Y;
+    const void *X;
+    const uint64_t *A_ptrs;
+    const uint64_t *B_ptrs;
+    int num_adapters, d_in, d_out;
+};
+
+struct LayerCall {
+    LayerProjIn p[kMaxProjections];
+    int num_projections;
+    const int32_t *seg_start;
+    const int32_t *seg_adapter;
+    int num_segments, M, r, dtype;
+    float scale;
+    void *workspace;
+    const int32_t *rows = nullptr;  // gathered call: token row of each segment row
+};
+
+// A layer call's workspace: each projection's fused workspace, back to back
+// at 256-byte aligned offsets, in projection order.
+inline size_t layer_workspace_total(const LayerProjIn *p, int num_projections, int num_segments, int M, int r,
+                                    int dtype) {
+    size_t total = 0;
+    for (int q = 0; q < num_projections; ++q)
+        total += align256(fused_layout(num_segments, M, p[q].d_in, r, dtype).total);
+    return total;
+}
+
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs &a, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t stream);
+hipError_t launch_fused_layer(const LayerCall &a, hipStream_t stream);
 
 }  // namespace sgmv

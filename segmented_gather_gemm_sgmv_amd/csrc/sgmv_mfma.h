@@ -53,11 +53,17 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
 // (the run is launched rounded up to a multiple of 8).
 constexpr int kXcds = 8;
 __host__ __device__ constexpr int round_up_xcds(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
-__device__ __forceinline__ int xcd_local_item(int first_id, int count) {
-    const int j = (int)blockIdx.x - first_id;
+// `id`: the workgroup's item id, congruent to its workgroup id modulo 8
+// (itself, or its offset inside a launch region that starts at a multiple
+// of 8).
+__device__ __forceinline__ int xcd_local_item(int id, int first_id, int count) {
+    const int j = id - first_id;
     const int per = (count + kXcds - 1) / kXcds;
-    const int item = ((int)blockIdx.x % kXcds) * per + j / kXcds;
+    const int item = (id % kXcds) * per + j / kXcds;
     return item < count ? item : -1;
+}
+__device__ __forceinline__ int xcd_local_item(int first_id, int count) {
+    return xcd_local_item((int)blockIdx.x, first_id, count);
 }
 
 __device__ __forceinline__ int clamp_to(int v, int M) { return v < 0 ? 0 : (v > M ? M : v); }

@@ -183,3 +183,52 @@ def test_pointer_table_keeps_pool_alive():
     del table
     gc.collect()
     assert ref() is None
+
+
+# -- the layer call --------------------------------------------------------------
+def projections(n=3, d_in=64, d_out=64, P=4, **over):
+    arr = (sg.SgmvProjection * max(n, 1))()
+    for q in range(n):
+        fields = dict(Y=P1 + q * 0x1000, X=P2 + q * 0x1000, A_ptrs=P3, B_ptrs=P6, num_adapters=P,
+                      d_in=d_in, d_out=d_out)
+        if q == n - 1:
+            fields.update(over)   # overrides land on the last projection
+        arr[q] = sg.SgmvProjection(**fields)
+    return arr
+
+
+def layer(arr=None, n=3, rows=None, ss=P4, sa=P5, N=2, M=4, r=16, dt=1, ws=0x800000, wsb=1 << 20):
+    arr = projections(n) if arr is None else arr
+    return sg.lib.sgmv_fused_layer(arr, n, rows, ss, sa, N, M, r, 32.0, dt, ws, wsb, None)
+
+
+def test_layer_argument_errors():
+    assert layer(r=12) == -3 and layer(dt=2) == -4
+    assert layer(n=9, arr=projections(9)) == -2 and layer(n=-1) == -2
+    assert sg.lib.sgmv_fused_layer(None, 2, None, P4, P5, 2, 4, 16, 32.0, 1, 0x800000, 1 << 20, None) == -1
+    assert layer(M=-1) == -2 and layer(N=-1) == -2
+    assert layer(arr=projections(3, num_adapters=-1)) == -2
+    assert layer(arr=projections(3, d_in=12)) == -2 and layer(arr=projections(3, d_out=0)) == -2
+    assert layer(arr=projections(3, Y=None)) == -1 and layer(arr=projections(3, X=None)) == -1
+    assert layer(arr=projections(3, A_ptrs=None)) == -1 and layer(arr=projections(3, B_ptrs=None)) == -1
+    assert layer(ss=None) == -1 and layer(sa=None) == -1
+    assert layer(arr=projections(3, Y=P1 + 8)) == -5
+    assert layer(ws=None) == -6 and layer(ws=0x800000 + 16) == -6
+
+
+def test_layer_empty_is_noop():
+    assert layer(n=0, arr=projections(0)) == 0
+    assert layer(M=0, ss=None, sa=None) == 0
+    assert layer(N=0, ss=None, sa=None) == 0
+    assert sg.lib.sgmv_fused_layer(None, 0, None, None, None, 2, 4, 16, 32.0, 1, None, 0, None) == 0
+
+
+def test_layer_workspace_is_the_sum_of_the_projections():
+    arr = projections(3, d_in=4096)
+    for q, d_in in enumerate((64, 1024, 4096)):
+        arr[q].d_in = d_in
+    total = sg.lib.sgmv_layer_workspace_bytes(arr, 3, 5, 300, 16, 1)
+    parts = [sg.lib.sgmv_workspace_bytes(5, 300, d, 64, 16, 1) for d in (64, 1024, 4096)]
+    assert total >= sum(parts) and total <= sum(parts) + 3 * 256 + 3 * (1 << 20)
+    assert layer(arr=arr, N=5, M=300, wsb=total - 1) == -6
+    assert sg.lib.sgmv_layer_workspace_bytes(arr, 9, 5, 300, 16, 1) == 0

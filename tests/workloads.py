@@ -171,6 +171,28 @@ def slice70b(seed: int = SEED_BASE + 5, M: int = 512, num_adapters: int = 2000, 
     return out
 
 
+# The seven projections of one 7B decoder layer: (name, d_in, d_out).
+LLAMA7B_PROJECTIONS = [
+    ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+    ("gate", 4096, 11008), ("up", 4096, 11008), ("down", 11008, 4096),
+]
+
+
+def layer7b(seed: int = SEED_BASE + 6, M: int = 64, num_adapters: int = 256, r: int = 16) -> List[Workload]:
+    """A whole 7B decoder layer at decode: 64 tokens, each a distinct adapter
+    from a pool of 256, through the layer's 7 projections; r = 16, alpha = 32,
+    bf16. Built like slice70b (pools not filled here)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = rng.choice(num_adapters, size=M, replace=False).astype(np.int32)
+    out = []
+    for pi, (name, d_in, d_out) in enumerate(LLAMA7B_PROJECTIONS):
+        w = Workload(f"layer7b_{name}", M, d_in, d_out, r, 2.0 * r, torch.bfloat16, num_adapters,
+                     segments_from_lengths([1] * M), ids.copy(), seed=seed * 100 + pi)
+        prng = np.random.Generator(np.random.PCG64(w.seed))
+        out.append(fill_tensors(w, prng, pool=False))
+    return out
+
+
 def device_pool(num_adapters: int, r: int, d: int, std: float, seed: int, device) -> torch.Tensor:
     """A P x r x d bf16 pool drawn on the device with a seeded torch generator
     (for pools too large to draw on the host)."""
@@ -239,4 +261,6 @@ ALL_CONFIGS: Dict[str, str] = {
     "decode_skewed": "d_in=4096, d_out=11008, r=16, alpha=32, 256 tokens, Zipf(1.5) over 64 adapters, sorted, bf16",
     "prefill": "d_in=d_out=4096, r=64, alpha=128, 8 segments of U{128..1024} rows, distinct adapters from 32, bf16",
     "slice70b": "7 projections of a 70B layer, 512 tokens, distinct adapters from 2000, r=16, alpha=32, bf16",
+    "layer7b": "7 projections of a 7B layer (q/k/v/o 4096->4096, gate/up 4096->11008, down 11008->4096), "
+               "64 decode tokens, distinct adapters from 256, r=16, alpha=32, bf16",
 }

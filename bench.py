@@ -15,7 +15,9 @@ row index (for decode_skewed the grouping's own permutation, for the other
 workloads a seeded shuffle); fused_permute is the comparison for those: torch
 row gathers of X and Y into segment order around the contiguous fused call,
 and a torch scatter of Y back. fused_layer runs all projections of a step
-(the 70B slice's seven) in one launch.
+(the 70B slice's seven) in one launch. per_segment is the schedule SGMV
+replaces: one fused launch per segment (each on its own rows and adapter),
+so a step costs one launch per segment instead of one in all.
 
 Prints ONE JSON line: value = algorithmic HBM GB/s (X read once, each
 segment's adapter read once, Y read and written once) over the timed steps,
@@ -83,7 +85,8 @@ def parse():
     p.add_argument("--workload", default="decode_distinct",
                    choices=["tiny", "decode_distinct", "decode_skewed", "prefill", "slice70b", "layer7b"])
     p.add_argument("--path", default="fused",
-                   choices=["split", "fused", "split_gather", "fused_gather", "fused_permute", "fused_layer"])
+                   choices=["split", "fused", "split_gather", "fused_gather", "fused_permute", "fused_layer",
+                            "per_segment"])
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,6 +115,22 @@ class Replica:
         self.rows64 = torch.from_numpy(rows.astype(np.int64)).to(dev)  # for torch's row permutes
         self.Xs = torch.empty_like(X)   # segment-order copies (fused_permute)
         self.Ys = torch.empty_like(Y)
+        self._segments = None
+
+    @property
+    def segments(self):
+        """per_segment: each segment as a batch of its own (rows a..b-1,
+        offsets [0, b - a], its adapter), built on first use."""
+        import torch
+        if self._segments is None:
+            w = self.w
+            self._segments = []
+            for s in range(w.num_segments):
+                a, b = int(w.seg_start[s]), int(w.seg_start[s + 1])
+                if b > a:
+                    meta = torch.tensor([0, b - a, int(w.seg_adapter[s])], dtype=torch.int32, device=self.X.device)
+                    self._segments.append((a, b, meta[:2], meta[2:]))
+        return self._segments
 
 
 def token_rows(w):
@@ -173,6 +192,12 @@ def step(group, path, ws=None):
     if path == "fused_layer":
         layer_call(group, ws)
         return
+    if path == "per_segment":
+        for rp in group:
+            for a, b, ss, sa in rp.segments:
+                sg.sgmv_fused(rp.Y[a:b], rp.X[a:b], rp.A_ptrs, rp.B_ptrs, ss, sa, rp.w.r, rp.w.alpha,
+                              workspace_buf=ws)
+        return
     for rp in group:
         w = rp.w
         if path == "fused":
@@ -210,7 +235,7 @@ def capture(reps, path, first, count, ws):
 
 KERNELS = {"fused": ["fused"], "split": ["shrink", "expand"], "fused_gather": ["fused_gather"],
            "split_gather": ["shrink_gather", "expand_scatter"], "fused_permute": ["fused"],
-           "fused_layer": ["fused_layer"]}
+           "fused_layer": ["fused_layer"], "per_segment": ["fused"]}
 
 
 def kernel_bytes(w, path):
@@ -223,6 +248,8 @@ def kernel_bytes(w, path):
     b = e * N * w.r * w.d_out
     y = 2 * e * w.M * w.d_out
     v = 4 * w.M * w.r
+    if path == "per_segment":  # one launch per segment: the average launch's bytes
+        return {"fused": (x + a + b + y) / max(1, N)}
     if path in ("fused", "fused_gather", "fused_permute", "fused_layer"):
         return {KERNELS[path][0]: x + a + b + y}
     names = KERNELS[path]
@@ -265,6 +292,9 @@ def time_kernels(reps, path, steps, wsbuf):
                 if name == "fused_layer":
                     layer_call(group, wsbuf)
                     continue
+                if path == "per_segment":
+                    step(group, path, wsbuf)
+                    continue
                 for rp in group:
                     launch_kernel(rp, name, wsbuf)
         g.replay()
@@ -277,7 +307,12 @@ def time_kernels(reps, path, steps, wsbuf):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        launches = n_replays * (len(reps) if name == "fused_layer" else sum(len(gr) for gr in reps))
+        if name == "fused_layer":
+            launches = n_replays * len(reps)
+        elif path == "per_segment":
+            launches = n_replays * sum(len(rp.segments) for gr in reps for rp in gr)
+        else:
+            launches = n_replays * sum(len(gr) for gr in reps)
         out[name] = a.elapsed_time(b) * 1e3 / launches   # microseconds per launch
         del g
     return out

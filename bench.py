@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--admission", action="store_true",
+                   help="also time adapter admission from pinned host memory (7B and 70B adapters)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this size (for counter scaling)")
     return p.parse_args()
@@ -318,6 +320,71 @@ def time_kernels(reps, path, steps, wsbuf):
     return out
 
 
+def admission_times(dev, reps=40):
+    """sgmv_admit_adapter from pinned host memory: one adapter of each shape
+    (every projection of a 7B and of a 70B layer, r = 16, bf16), copied into
+    a spare device slot and pointed at by a table entry; `reps` admissions per
+    shape, bracketed by HIP events on the stream they are enqueued on."""
+    import torch
+    import segmented_gather_gemm_sgmv_amd as sg
+    from tests import workloads as wl
+    out = {}
+    for layer, projs in (("7b", wl.LLAMA7B_PROJECTIONS), ("70b", wl.LLAMA70B_PROJECTIONS)):
+        r = 16
+        slots, hosts, tables = [], [], []
+        nbytes = 0
+        for _, d_in, d_out in projs:
+            A = torch.empty((r, d_in), dtype=torch.bfloat16, device=dev)
+            B = torch.empty((r, d_out), dtype=torch.bfloat16, device=dev)
+            Ah = torch.empty((r, d_in), dtype=torch.bfloat16, pin_memory=True).normal_()
+            Bh = torch.empty((r, d_out), dtype=torch.bfloat16, pin_memory=True).normal_()
+            slots.append((A, B))
+            hosts.append((Ah, Bh))
+            tables.append((torch.zeros(4, dtype=torch.int64, device=dev), torch.zeros(4, dtype=torch.int64, device=dev)))
+            nbytes += 2 * r * (d_in + d_out)
+        def admit_all():
+            for (A, B), (Ah, Bh), (ta, tb) in zip(slots, hosts, tables):
+                sg.sgmv_admit_adapter(A, B, Ah, Bh, ta, tb, 1)
+        admit_all()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            admit_all()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[f"layer{layer}_adapter"] = {"projections": len(projs), "bytes": nbytes, "ms": ms,
+                                        "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+        del slots, hosts, tables
+    # a whole 7B adapter (32 layers x 7 projections, r = 16) held as one slab
+    # pair (all A matrices, all B matrices), admitted with one call
+    r, layers = 16, 32
+    a_elems = layers * r * sum(d_in for _, d_in, _ in wl.LLAMA7B_PROJECTIONS)
+    b_elems = layers * r * sum(d_out for _, _, d_out in wl.LLAMA7B_PROJECTIONS)
+    A = torch.empty(a_elems, dtype=torch.bfloat16, device=dev)
+    B = torch.empty(b_elems, dtype=torch.bfloat16, device=dev)
+    Ah = torch.empty(a_elems, dtype=torch.bfloat16, pin_memory=True).normal_()
+    Bh = torch.empty(b_elems, dtype=torch.bfloat16, pin_memory=True).normal_()
+    ta, tb = torch.zeros(4, dtype=torch.int64, device=dev), torch.zeros(4, dtype=torch.int64, device=dev)
+    sg.sgmv_admit_adapter(A, B, Ah, Bh, ta, tb, 1)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    a.record(stream)
+    for _ in range(n):
+        sg.sgmv_admit_adapter(A, B, Ah, Bh, ta, tb, 1)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    nbytes = 2 * (a_elems + b_elems)
+    out["whole7b_adapter_one_slab"] = {"layers": layers, "bytes": nbytes, "ms": ms,
+                                       "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+    return out
+
+
 def cpu_baseline(ws, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload:
     whole batches of the first projection, repeated for about `seconds`."""
@@ -452,6 +519,8 @@ def main():
                      "traffic": profiled_traffic(args.workload, args.path, dom),
                      "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
     }
+    if args.admission:
+        out["admission"] = admission_times(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -255,6 +255,30 @@ int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
 int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,
                        int64_t slot_bytes);
 
+/*
+ * Adapter admission (Punica guide, "Core Innovation 2": the hot adapters live
+ * in one unified device pool, and a cold one is copied in from host memory
+ * on demand, in under 1.5 ms per adapter over the host link).
+ *
+ * Enqueues on `stream`, in this order: the copy of A_bytes from A_host to
+ * the device slot A_slot, the copy of B_bytes from B_host to B_slot, and the
+ * update A_ptrs[slot] = A_slot, B_ptrs[slot] = B_slot (a one-workgroup
+ * kernel). An SGMV call enqueued after it on the same stream uses the new
+ * adapter; one enqueued before it uses the old entries. The caller keeps
+ * A_host and B_host unchanged until the copies complete; with pinned host
+ * memory (hipHostMalloc) the call returns at once, with pageable memory the
+ * runtime may finish the copy before returning.
+ *
+ * A_slot, B_slot  device memory of A_bytes / B_bytes, 16-byte aligned: A_k
+ *                 as r rows of d_in, B_k as r rows of d_out (the layout above).
+ * slot            0 <= slot < num_adapters (the table length).
+ * Returns SGMV_ERR_NULL, _SHAPE (slot out of range, zero bytes), _ALIGN or
+ * _HIP; nothing is enqueued on error.
+ */
+int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const void *B_host,
+                       size_t A_bytes, size_t B_bytes, uint64_t *A_ptrs, uint64_t *B_ptrs,
+                       int32_t slot, int32_t num_adapters, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *sgmv_status_string(int status);
 

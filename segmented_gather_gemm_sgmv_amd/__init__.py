@@ -45,6 +45,7 @@ EXPORTS = {
     "sgmv_fused_layer": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                         _vp]),
     "sgmv_layer_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
+    "sgmv_admit_adapter": (ctypes.c_int, [_vp, _vp, _vp, _vp, _sz, _sz, _vp, _vp, _i32, _i32, _vp]),
     "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
@@ -342,12 +343,34 @@ def sgmv_pool_pointers(pool: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def sgmv_admit_adapter(A_slot: torch.Tensor, B_slot: torch.Tensor, A_host: torch.Tensor, B_host: torch.Tensor,
+                       A_ptrs: torch.Tensor, B_ptrs: torch.Tensor, slot: int, stream=None) -> None:
+    """Copy an adapter from host memory into device slots A_slot (r x d_in)
+    and B_slot (r x d_out), then point table entry `slot` at them, all in
+    stream order. A_host / B_host: CPU tensors of the slots' shape and dtype
+    (pinned for an asynchronous copy); keep them alive and unchanged until the
+    stream reaches the copy."""
+    for name, dev_t, host_t in (("A", A_slot, A_host), ("B", B_slot, B_host)):
+        if host_t.device.type != "cpu" or not host_t.is_contiguous():
+            raise ValueError(f"{name}_host must be a contiguous CPU tensor")
+        if host_t.shape != dev_t.shape or host_t.dtype != dev_t.dtype:
+            raise ValueError(f"{name}_host must match {name}_slot in shape and dtype")
+    if A_ptrs.numel() != B_ptrs.numel():
+        raise ValueError("A_ptrs and B_ptrs must have one entry per adapter")
+    st = lib.sgmv_admit_adapter(_dev(A_slot, "A_slot"), _dev(B_slot, "B_slot"), A_host.data_ptr(),
+                                B_host.data_ptr(), A_host.numel() * A_host.element_size(),
+                                B_host.numel() * B_host.element_size(), _dev(A_ptrs, "A_ptrs", torch.int64, 1),
+                                _dev(B_ptrs, "B_ptrs", torch.int64, 1), int(slot), A_ptrs.numel(),
+                                _stream(A_slot, stream))
+    _check("sgmv_admit_adapter", st)
+
+
 def sgmv_version() -> int:
     return int(lib.sgmv_version())
 
 
 __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sgmv_expand_scatter",
            "sgmv_fused_gather", "sgmv_fused_layer", "sgmv_layer_workspace_bytes", "SgmvProjection",
-           "SGMV_MAX_PROJECTIONS", "sgmv_workspace_bytes", "sgmv_build_segments",
+           "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16"]

@@ -275,6 +275,19 @@ int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
     return SGMV_OK;
 }
 
+int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const void *B_host,
+                       size_t A_bytes, size_t B_bytes, uint64_t *A_ptrs, uint64_t *B_ptrs,
+                       int32_t slot, int32_t num_adapters, void *stream) {
+    if (!A_slot || !B_slot || !A_host || !B_host || !A_ptrs || !B_ptrs) return SGMV_ERR_NULL;
+    if (slot < 0 || slot >= num_adapters || A_bytes == 0 || B_bytes == 0) return SGMV_ERR_SHAPE;
+    if (!aligned16(A_slot) || !aligned16(B_slot)) return SGMV_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(A_slot, A_host, A_bytes, hipMemcpyHostToDevice, st) != hipSuccess) return SGMV_ERR_HIP;
+    if (hipMemcpyAsync(B_slot, B_host, B_bytes, hipMemcpyHostToDevice, st) != hipSuccess) return SGMV_ERR_HIP;
+    return hip_status(sgmv::launch_set_slot(A_ptrs, B_ptrs, slot, reinterpret_cast<uintptr_t>(A_slot),
+                                            reinterpret_cast<uintptr_t>(B_slot), st));
+}
+
 int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,
                        int64_t slot_bytes) {
     if (num_adapters < 0 || slot_bytes < 0) return SGMV_ERR_SHAPE;

@@ -987,6 +987,21 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
     SGMV_RANK_SWITCH(launch_fused_t, bf16_t, a, st)
 }
 
+// One pool slot's table entries, written by one lane (vector stores).
+__global__ __launch_bounds__(kWave) void set_slot_kernel(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot,
+                                                        uint64_t a, uint64_t b) {
+    if (threadIdx.x == 0) {
+        A_ptrs[slot] = a;
+        B_ptrs[slot] = b;
+    }
+}
+
+hipError_t launch_set_slot(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot, uint64_t a, uint64_t b,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(set_slot_kernel, dim3(1), dim3(kWave), 0, st, A_ptrs, B_ptrs, slot, a, b);
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_layer_t, float, a, st)
     SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_t, a, st)

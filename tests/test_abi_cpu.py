@@ -232,3 +232,15 @@ def test_layer_workspace_is_the_sum_of_the_projections():
     assert total >= sum(parts) and total <= sum(parts) + 3 * 256 + 3 * (1 << 20)
     assert layer(arr=arr, N=5, M=300, wsb=total - 1) == -6
     assert sg.lib.sgmv_layer_workspace_bytes(arr, 9, 5, 300, 16, 1) == 0
+
+
+def admit(A_slot=P1, B_slot=P2, A_host=P3, B_host=P4, Ab=1024, Bb=2048, A_ptrs=P5, B_ptrs=P6, slot=1, P=4):
+    return sg.lib.sgmv_admit_adapter(A_slot, B_slot, A_host, B_host, Ab, Bb, A_ptrs, B_ptrs, slot, P, None)
+
+
+def test_admit_argument_errors():
+    for k in ("A_slot", "B_slot", "A_host", "B_host", "A_ptrs", "B_ptrs"):
+        assert admit(**{k: None}) == -1
+    assert admit(slot=-1) == -2 and admit(slot=4) == -2 and admit(P=0, slot=0) == -2
+    assert admit(Ab=0) == -2 and admit(Bb=0) == -2
+    assert admit(A_slot=P1 + 8) == -5 and admit(B_slot=P2 + 4) == -5

@@ -10,8 +10,14 @@ constexpr int kWave = 64;
 constexpr int kBlockThreads = 256;  // threads per workgroup in every kernel (4 waves)
 
 // Storage element types. bf16 is kept as raw 16-bit patterns and widened by a
-// shift; fp32 is used as is.
+// shift; fp32 is used as is. bf16_short_t is bf16 storage for batches whose
+// segments are all too short for the matrix-core path: kernels built for it
+// leave that path out (its code, LDS and registers), and any segment runs on
+// the vector path, which is correct for every length.
 struct bf16_t {
+    uint16_t bits;
+};
+struct bf16_short_t {
     uint16_t bits;
 };
 
@@ -20,12 +26,17 @@ struct Elem;
 template <>
 struct Elem<float> {
     static constexpr int kPerVec = 4;  // elements per 16-byte vector
-    static constexpr bool kIsBf16 = false;
+    static constexpr bool kMfma = false;  // long segments take the MFMA path
 };
 template <>
 struct Elem<bf16_t> {
     static constexpr int kPerVec = 8;
-    static constexpr bool kIsBf16 = true;
+    static constexpr bool kMfma = true;
+};
+template <>
+struct Elem<bf16_short_t> {
+    static constexpr int kPerVec = 8;
+    static constexpr bool kMfma = false;
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -71,6 +82,11 @@ __device__ __forceinline__ void widen<bf16_t>(uint4 v, float (&out)[8]) {
     }
 }
 
+template <>
+__device__ __forceinline__ void widen<bf16_short_t>(uint4 v, float (&out)[8]) {
+    widen<bf16_t>(v, out);
+}
+
 // Narrow fp32 values to one 16-byte vector, rounding to nearest-even.
 template <typename T>
 __device__ __forceinline__ uint4 narrow(const float (&in)[Elem<T>::kPerVec]);
@@ -92,6 +108,11 @@ template <>
 __device__ __forceinline__ uint4 narrow<bf16_t>(const float (&in)[8]) {
     return make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
                       pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
+}
+
+template <>
+__device__ __forceinline__ uint4 narrow<bf16_short_t>(const float (&in)[8]) {
+    return narrow<bf16_t>(in);
 }
 
 // Adapter address lookup for one wave. The address of a segment's adapter

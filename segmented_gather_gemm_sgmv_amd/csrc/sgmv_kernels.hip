@@ -197,7 +197,7 @@ __device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, ArowFn
 
 template <typename T>
 __device__ __forceinline__ bool takes_mfma(int rows) {
-    return Elem<T>::kIsBf16 && rows >= kLongRows;
+    return Elem<T>::kMfma && rows >= kLongRows;
 }
 
 // Whether the vector path owns a segment: rows present, a valid adapter, and
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
                                                    s, j, M, d_in, lane, rm);
         return;
     }
-    if constexpr (Elem<T>::kIsBf16) {
+    if constexpr (Elem<T>::kMfma) {
         __shared__ ShrinkSmem<R> sm;
         __shared__ PieceList pl;
         __shared__ int s_flag;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
                                                        s, n0, M, d_out, scale, lo, hi, []() { return true; }, rm);
         return;
     }
-    if constexpr (Elem<T>::kIsBf16) {
+    if constexpr (Elem<T>::kMfma) {
         __shared__ ExpandSmem<R> sm;
         __shared__ PieceList pl;
         const int e = xcd_local_item(gemv_items, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
@@ -729,7 +729,7 @@ __device__ __forceinline__ void fused_item(
         }
         return;
     }
-    if constexpr (Elem<T>::kIsBf16) {
+    if constexpr (Elem<T>::kMfma) {
         __shared__ union {
             ShrinkSmem<R> shrink;
             ExpandSmem<R> expand;
@@ -848,8 +848,9 @@ static int gemv_col_tiles(int d_out) {
 template <typename T, int R, bool kGather>
 static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
+    const int tiles = Elem<T>::kMfma ? L.tiles : 0;
     const unsigned grid =
-        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)L.tiles * L.ks;
+        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)tiles * L.ks;
     char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
@@ -868,7 +869,7 @@ static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
 template <typename T, int R, bool kGather>
 static hipError_t launch_expand_g(const ExpandArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
-    const int tiles = mfma_tiles(a.dtype, a.M);
+    const int tiles = Elem<T>::kMfma ? mfma_tiles(a.dtype, a.M) : 0;
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     // Batches of short segments (under 16 rows on average) run mostly on the
@@ -895,18 +896,19 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
 template <typename T, int R, bool kGather>
 static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
     const FusedLayout L = fused_layout(a.num_segments, a.M, a.d_in, a.r, a.dtype);
+    const int tiles = Elem<T>::kMfma ? L.tiles : 0;
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
-    const int ntiles_m = L.tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
-                          (unsigned)L.tiles * L.ks +
-                          (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(L.tiles * ntiles_m);
+                          (unsigned)tiles * L.ks +
+                          (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
     hipLaunchKernelGGL((fused_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, L.tiles, L.ks, a.scale,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, L.ks, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), seg_c, tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
                        reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M});
@@ -936,9 +938,10 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         d.num_adapters = in.num_adapters;
         d.d_in = in.d_in;
         d.d_out = in.d_out;
+        const int tiles = Elem<T>::kMfma ? FL.tiles : 0;
         d.ntiles_g = gemv_col_tiles<T>(in.d_out);
-        d.ntiles_m = FL.tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
-        d.num_tiles = FL.tiles;
+        d.ntiles_m = tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+        d.num_tiles = tiles;
         d.ks = FL.ks;
         char *w = ws + ws_off;
         d.seg_counters = reinterpret_cast<uint32_t *>(w + FL.seg_counters);
@@ -946,8 +949,8 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         d.Vws = reinterpret_cast<float *>(w + FL.v);
         d.Vpairs = reinterpret_cast<float *>(w + FL.vpairs);
         d.partials = reinterpret_cast<float *>(w + FL.partials);
-        d.items = round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + FL.tiles * FL.ks +
-                  a.num_segments * d.ntiles_g + round_up_xcds(FL.tiles * d.ntiles_m);
+        d.items = round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + tiles * FL.ks +
+                  a.num_segments * d.ntiles_g + round_up_xcds(tiles * d.ntiles_m);
         d.base = base;
         base += round_up_xcds(d.items);
         ws_off += align256(FL.total);
@@ -972,18 +975,30 @@ static hipError_t launch_fused_layer_t(const LayerCall &a, hipStream_t st) {
         default: return hipErrorInvalidValue;       \
     }
 
+// Whether a bf16 batch can hold a segment long enough for the MFMA path:
+// with every segment non-empty, the longest has M - N + 1 rows. Batches of
+// decode tokens (one or a few rows per segment) cannot, and take kernels
+// built without that path. Should empty segments leave a longer one after
+// all, the vector path computes it.
+static bool long_segments_possible(int M, int num_segments) {
+    return (int64_t)M - num_segments + 1 >= kLongRows;
+}
+
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_shrink_t, float, a, st)
+    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_shrink_t, bf16_short_t, a, st)
     SGMV_RANK_SWITCH(launch_shrink_t, bf16_t, a, st)
 }
 
 hipError_t launch_expand(const ExpandArgs &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_expand_t, float, a, st)
+    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_expand_t, bf16_short_t, a, st)
     SGMV_RANK_SWITCH(launch_expand_t, bf16_t, a, st)
 }
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_t, float, a, st)
+    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_fused_t, bf16_short_t, a, st)
     SGMV_RANK_SWITCH(launch_fused_t, bf16_t, a, st)
 }
 
@@ -1004,6 +1019,8 @@ hipError_t launch_set_slot(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot, uint64_
 
 hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
     if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_layer_t, float, a, st)
+    if (!long_segments_possible(a.M, a.num_segments))
+        SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_short_t, a, st)
     SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_t, a, st)
 }
 

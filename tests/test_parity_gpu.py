@@ -488,3 +488,27 @@ def test_one_call_per_segment_equals_one_call(dev, oracle, name):
         else:
             _, Y_ref = oracle_run(oracle, w)
             assert_close(Y_seg, Y_ref, what=f"{name} per segment")
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_long_segment_among_empty_ones(dev, oracle, r):
+    """bf16 batches where every segment could be short (M - N + 1 < 16) run on
+    kernels built without the MFMA path; empty segments can still leave one
+    long segment, which the vector path must compute, in every call."""
+    rng = np.random.Generator(np.random.PCG64(120 + r))
+    lengths = [0] * 14 + [37] + [0] * 10 + [1, 2]      # M = 40, N = 27: M - N + 1 = 14
+    ids = rng.integers(0, 6, size=len(lengths)).astype(np.int32)
+    w = wl.Workload("empty_and_long", int(sum(lengths)), 2056, 1032, r, 2.0 * r, torch.bfloat16, 6,
+                    wl.segments_from_lengths(lengths), ids)
+    wl.fill_tensors(w, rng)
+    w.Y = wl._normal(rng, (w.M, w.d_out), 1.0, w.dtype)
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    V, Y = run_split(c)
+    assert_close(V, V_ref, what="V")
+    assert_close(Y, Y_ref, what="split Y")
+    assert_close(run_fused(c), Y_ref, what="fused Y")
+    Yl = c.Y0.clone()
+    sg.sgmv_fused_layer([(Yl, c.X, c.A_ptrs, c.B_ptrs)], c.seg_start, c.seg_adapter, w.r, w.alpha)
+    torch.cuda.synchronize()
+    assert_close(Yl, Y_ref, what="layer Y")

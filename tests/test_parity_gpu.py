@@ -512,3 +512,48 @@ def test_long_segment_among_empty_ones(dev, oracle, r):
     sg.sgmv_fused_layer([(Yl, c.X, c.A_ptrs, c.B_ptrs)], c.seg_start, c.seg_adapter, w.r, w.alpha)
     torch.cuda.synchronize()
     assert_close(Yl, Y_ref, what="layer Y")
+
+
+def _sampled_oracle(oracle, w, rows):
+    """The oracle on chosen rows of w only: each row becomes a segment of its
+    own with its segment's adapter."""
+    ids = pins.row_adapter(w.seg_start, w.seg_adapter, w.M)[rows].astype(np.int32)
+    sub = wl.Workload(w.name, len(rows), w.d_in, w.d_out, w.r, w.alpha, w.dtype, w.num_adapters,
+                      wl.segments_from_lengths([1] * len(rows)), ids, X=w.X[torch.from_numpy(rows)],
+                      Y=w.Y[torch.from_numpy(rows)], A_pool=w.A_pool, B_pool=w.B_pool)
+    return oracle_run(oracle, sub)
+
+
+def test_large_batch(dev, oracle):
+    """40,000 rows (X and Y of 328 MB each): segments spanning hundreds of
+    64-row tiles next to short ones, every call, checked on sampled rows of
+    every segment (its first and last rows and random ones)."""
+    rng = np.random.Generator(np.random.PCG64(130))
+    lengths = [20000, 1, 15, 16, 9000, 0, 10968]
+    ids = np.array([3, 0, 2, 1, 4, 2, 0], np.int32)
+    w = wl.Workload("large", int(sum(lengths)), 4096, 4096, 16, 32.0, torch.bfloat16, 5,
+                    wl.segments_from_lengths(lengths), ids)
+    wl.fill_tensors(w, rng)
+    rows = set()
+    for s in range(len(lengths)):
+        a, b = int(w.seg_start[s]), int(w.seg_start[s + 1])
+        if b > a:
+            rows |= {a, b - 1} | set(rng.integers(a, b, size=min(6, b - a)).tolist())
+    rows = np.array(sorted(rows), np.int64)
+    print(f"large batch: M={w.M}, {len(rows)} sampled rows", flush=True)
+    c = to_device(w, dev)
+    V_ref, Y_ref = _sampled_oracle(oracle, w, rows)
+    r_t = torch.from_numpy(rows).to(dev)
+    V, Y = run_split(c)
+    assert_close(V[r_t], V_ref, what="V")
+    assert_close(Y[r_t], Y_ref, what="split Y")
+    assert_close(run_fused(c)[r_t], Y_ref, what="fused Y")
+    perm = rng.permutation(w.M).astype(np.int32)
+    rows_t = torch.from_numpy(perm).to(dev)
+    Xg = torch.empty_like(c.X)
+    Xg[rows_t.long()] = c.X   # token perm[p] holds segment row p
+    Yg = torch.empty_like(c.Y0)
+    Yg[rows_t.long()] = c.Y0
+    sg.sgmv_fused_gather(Yg, Xg, rows_t, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
+    torch.cuda.synchronize()
+    assert_close(Yg[rows_t.long()][r_t], Y_ref, what="fused_gather Y")

@@ -58,7 +58,7 @@ size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32
         !valid_dtype(dtype))
         return 0;
     return std::max(sgmv::shrink_layout(M, d_in, r, dtype).total,
-                    sgmv::fused_layout(num_segments, M, d_in, r, dtype).total);
+                    sgmv::fused_layout(M, d_in, d_out, r, dtype).total);
 }
 
 namespace {
@@ -123,7 +123,7 @@ int fused_call(void *Y, const void *X, const int32_t *rows, bool gathered, const
         return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
     st = check_workspace(workspace, workspace_bytes,
-                         sgmv::fused_layout(num_segments, M, d_in, r, dtype).total);
+                         sgmv::fused_layout(M, d_in, d_out, r, dtype).total);
     if (st != SGMV_OK) return st;
     sgmv::FusedArgs a{Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
                       num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, workspace,

@@ -112,9 +112,12 @@ __device__ __forceinline__ bool poll_v_block(const float *V, int row0, int nrows
 // the block repeat the last row and are simply not stored. Straight-line
 // loads let the compiler keep all of them in flight at once.
 // ----------------------------------------------------------------------------
+// kFlagged: V holds `copies` copies of M x r flagged pairs, `copy_stride`
+// pairs apart, and each result goes to every copy.
 template <typename T, int R, int ROWS, bool kFlagged, typename ArowFn, typename RM>
 __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
-                                            int row0, int nrows, int j, int lane, RM rm) {
+                                            int row0, int nrows, int j, int lane, RM rm, int copies,
+                                            size_t copy_stride) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int U = ROWS <= 2 ? kShrinkUnroll : (ROWS <= 4 ? kShrinkUnroll / 2 : kShrinkUnroll / 4);
     const int nvec = d_in / VEC;
@@ -168,9 +171,9 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
         const int m = lane / kSpread;
         const size_t idx = (size_t)(row0 + m) * R + j;
         if (m < nrows) {
-            if constexpr (kFlagged)
-                store_v_flagged(V, idx, acc[0]);
-            else
+            if constexpr (kFlagged) {
+                for (int c = 0; c < copies; ++c) store_v_flagged(V, idx + (size_t)c * copy_stride, acc[0]);
+            } else
                 V[idx] = acc[0];
         }
     }
@@ -181,17 +184,22 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
 // row p.
 template <typename T, int R, bool kFlagged, typename ArowFn, typename RM>
 __device__ __forceinline__ void shrink_segment_wave(float *V, const T *X, ArowFn arow_fn, int d_in,
-                                                    int lo, int hi, int j, int lane, RM rm) {
+                                                    int lo, int hi, int j, int lane, RM rm, int copies,
+                                                    size_t copy_stride) {
     for (int row0 = lo; row0 < hi; row0 += kRowBlock) {
         const int nrows = min(kRowBlock, hi - row0);
         if (nrows == 1)
-            shrink_wave<T, R, 1, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
+            shrink_wave<T, R, 1, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm, copies,
+                                                copy_stride);
         else if (nrows <= 2)
-            shrink_wave<T, R, 2, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
+            shrink_wave<T, R, 2, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm, copies,
+                                                copy_stride);
         else if (nrows <= 4)
-            shrink_wave<T, R, 4, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
+            shrink_wave<T, R, 4, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm, copies,
+                                                copy_stride);
         else
-            shrink_wave<T, R, 8, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm);
+            shrink_wave<T, R, 8, kFlagged>(V, X, arow_fn, d_in, row0, nrows, j, lane, rm, copies,
+                                                copy_stride);
     }
 }
 
@@ -216,7 +224,7 @@ template <typename T, int R, bool kFlagged, bool kSpec, typename RM>
 __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int j, int M,
-                                                   int d_in, int lane, RM rm) {
+                                                   int d_in, int lane, RM rm, int copies = 1) {
     AdapterTable<kSpec> tab;
     tab.load(A_ptrs, num_adapters, lane);
     int lo, hi;
@@ -224,7 +232,7 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     segment_rows(seg_start, s, M, lo, hi);
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
-    shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane, rm);
+    shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane, rm, copies, (size_t)M * R);
     return true;
 }
 
@@ -669,15 +677,14 @@ __device__ __forceinline__ void fused_item(
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
+    int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
     float *Vpairs, float *partials, RowMap<kGather> rm, const int item) {
-    // each segment and each 64-row tile owns one cache line of counters. A
-    // segment's word 1 counts expand departures (the vector path hands V over
-    // as flagged pairs, Vpairs). A tile's word 0 counts the shrink parts
-    // whose V entries are stored (polled by the expand workgroups until it
-    // reaches ks), word 1 counts expand departures, word 2 synchronises the
-    // parts of a split shrink.
-    uint32_t *const seg_depart = seg_counters + 1;
+    // The vector path hands V over as flagged pairs (Vpairs), one copy per
+    // expand column tile, so each expand workgroup clears its own copy with
+    // no counter. Each 64-row tile owns one cache line of counters: word 0
+    // counts the shrink parts whose V entries are stored (polled by the
+    // expand workgroups until it reaches ks), word 1 counts expand
+    // departures, word 2 synchronises the parts of a split shrink.
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
     uint32_t *const tile_split = tile_counters + 2;
@@ -696,10 +703,10 @@ __device__ __forceinline__ void fused_item(
         const int j = grp * kWavesPerBlock + tid / kWave;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                 s, j, M, d_in, tid & (kWave - 1), rm);
+                                                 s, j, M, d_in, tid & (kWave - 1), rm, ntiles_g);
         else
             shrink_vector_item<T, R, true, false>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, tid & (kWave - 1), rm);
+                                                  s, j, M, d_in, tid & (kWave - 1), rm, ntiles_g);
         return;
     }
     if (item >= a1 && item < a2) {
@@ -707,26 +714,24 @@ __device__ __forceinline__ void fused_item(
         const int s = e / ntiles_g;
         const int tile = e % ntiles_g;
         const int n0 = (tile * kBlock + tid) * VEC;
+        float *const Vcopy = Vpairs + (size_t)tile * M * R * 2;  // this column tile's copy (pairs)
         int lo, hi;
         auto ready = []() { return true; };  // the V reads wait for their flags
         // here B is requested before V is waited for, so B_k's address is on
         // the critical path: read the table early when the pool is small
         const bool valid =
             num_adapters <= kSpecTable
-                ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
+                ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vcopy, B_ptrs, num_adapters, seg_start,
                                                                  seg_adapter, s, n0, M, d_out, scale,
                                                                  lo, hi, ready, rm)
-                : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vpairs, B_ptrs, num_adapters, seg_start,
+                : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vcopy, B_ptrs, num_adapters, seg_start,
                                                                   seg_adapter, s, n0, M, d_out, scale,
                                                                   lo, hi, ready, rm);
         if (!valid) return;
-        if (depart_last(&seg_depart[s * kCounterStride], (uint32_t)ntiles_g, &s_flag)) {
-            // last one out: return the segment's V pairs and its counter to zero
-            zero_pairs(Vpairs, lo, hi, R);
-            if (tid == 0)
-                __hip_atomic_store(&seg_depart[s * kCounterStride], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+        // every wave of this workgroup has read its values: clear the copy
+        // (no other workgroup reads it)
+        __syncthreads();
+        zero_pairs(Vcopy, lo, hi, R);
         return;
     }
     if constexpr (Elem<T>::kMfma) {
@@ -799,11 +804,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int ks, float scale, int long_batch, uint32_t *seg_counters, uint32_t *tile_counters, float *Vws,
+    int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
     float *Vpairs, float *partials, RowMap<kGather> rm) {
     fused_item<T, R, kGather>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
                               d_in, d_out, ntiles_g, ntiles_m, num_tiles, ks, scale, long_batch,
-                              seg_counters, tile_counters, Vws, Vpairs, partials, rm, (int)blockIdx.x);
+                              tile_counters, Vws, Vpairs, partials, rm, (int)blockIdx.x);
 }
 
 // Layer-batched fused launch (the launch accounting of the Punica guide's
@@ -827,7 +832,7 @@ __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
     fused_item<T, R, kGather>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
                               d.B_ptrs, d.num_adapters, seg_start, seg_adapter, num_segments, M, d.d_in,
                               d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.ks, scale, long_batch,
-                              d.seg_counters, d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, item);
+                              d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, item);
 }
 
 // ----------------------------------------------------------------------------
@@ -895,21 +900,21 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
 
 template <typename T, int R, bool kGather>
 static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
-    const FusedLayout L = fused_layout(a.num_segments, a.M, a.d_in, a.r, a.dtype);
+    const FusedLayout L = fused_layout(a.M, a.d_in, a.d_out, a.r, a.dtype);
     const int tiles = Elem<T>::kMfma ? L.tiles : 0;
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    if (ntiles_g != L.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
                           (unsigned)tiles * L.ks +
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
-    uint32_t *seg_c = reinterpret_cast<uint32_t *>(ws + L.seg_counters);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
     hipLaunchKernelGGL((fused_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
                        a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, L.ks, a.scale,
-                       (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), seg_c, tile_c,
+                       (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
                        reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M});
     return hipGetLastError();
@@ -929,7 +934,7 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
     int base = 0;
     for (int q = 0; q < a.num_projections; ++q) {
         const LayerProjIn &in = a.p[q];
-        const FusedLayout FL = fused_layout(a.num_segments, a.M, in.d_in, a.r, a.dtype);
+        const FusedLayout FL = fused_layout(a.M, in.d_in, in.d_out, a.r, a.dtype);
         LayerProj &d = L.p[q];
         d.Y = in.Y;
         d.X = in.X;
@@ -940,11 +945,11 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         d.d_out = in.d_out;
         const int tiles = Elem<T>::kMfma ? FL.tiles : 0;
         d.ntiles_g = gemv_col_tiles<T>(in.d_out);
+        if (d.ntiles_g != FL.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
         d.ntiles_m = tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
         d.num_tiles = tiles;
         d.ks = FL.ks;
         char *w = ws + ws_off;
-        d.seg_counters = reinterpret_cast<uint32_t *>(w + FL.seg_counters);
         d.tile_counters = reinterpret_cast<uint32_t *>(w + FL.tile_counters);
         d.Vws = reinterpret_cast<float *>(w + FL.v);
         d.Vpairs = reinterpret_cast<float *>(w + FL.vpairs);

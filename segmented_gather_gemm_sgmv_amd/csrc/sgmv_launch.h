@@ -93,29 +93,37 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     return L;
 }
 
-// Fused workspace: one 128-byte line of counters per segment (expand
-// workgroups departed) and per 64-row tile (V complete, expand workgroups
-// departed, split shrink parts arrived), so that consumers polling one tile
-// do not contend with another's; then V of the MFMA path (M x r fp32), the
-// split partials as above, and V of the vector path as M x r flagged 64-bit
-// pairs. Every launch leaves it all zero.
+// Columns of Y one vector-path expand workgroup covers: 256 threads, one
+// 16-byte vector each.
+inline int vector_col_tiles(int d_out, int dtype) {
+    const int cols = 256 * (dtype == kBF16 ? 8 : 4);
+    return (d_out + cols - 1) / cols;
+}
+
+// Fused workspace: one 128-byte line of counters per 64-row tile (V
+// complete, expand workgroups departed, split shrink parts arrived), so
+// that consumers polling one tile do not contend with another's; then V of
+// the MFMA path (M x r fp32), the split partials as above, and V of the
+// vector path as flagged 64-bit pairs, one M x r copy per vector expand
+// column tile (each expand workgroup reads and clears its own copy). Every
+// launch leaves it all zero.
 struct FusedLayout {
-    size_t seg_counters, tile_counters, v, partials, vpairs, total;
-    int tiles, ks;
+    size_t tile_counters, v, partials, vpairs, total;
+    int tiles, ks, copies;
 };
 
-inline FusedLayout fused_layout(int num_segments, int M, int d_in, int r, int dtype) {
+inline FusedLayout fused_layout(int M, int d_in, int d_out, int r, int dtype) {
     FusedLayout L;
     L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
-    L.seg_counters = 0;
-    L.tile_counters = kCounterStride * sizeof(uint32_t) * (size_t)num_segments;
-    L.v = align256(L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
+    L.copies = vector_col_tiles(d_out, dtype);
+    L.tile_counters = 0;
+    L.v = align256(kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
     L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
     L.vpairs = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.tiles * L.ks *
                                                      kTileRows64 * (size_t)std::max(r, 16)
                                                : 0));
-    L.total = align256(L.vpairs + sizeof(uint64_t) * (size_t)M * (size_t)r);
+    L.total = align256(L.vpairs + sizeof(uint64_t) * (size_t)M * (size_t)r * (size_t)L.copies);
     return L;
 }
 
@@ -130,7 +138,7 @@ struct LayerProj {
     const void *X;
     const uint64_t *A_ptrs;
     const uint64_t *B_ptrs;
-    uint32_t *seg_counters, *tile_counters;
+    uint32_t *tile_counters;
     float *Vws, *Vpairs, *partials;
     int num_adapters, d_in, d_out;
     int ntiles_g, ntiles_m, num_tiles, ks;
@@ -168,7 +176,7 @@ inline size_t layer_workspace_total(const LayerProjIn *p, int num_projections, i
                                     int dtype) {
     size_t total = 0;
     for (int q = 0; q < num_projections; ++q)
-        total += align256(fused_layout(num_segments, M, p[q].d_in, r, dtype).total);
+        total += align256(fused_layout(M, p[q].d_in, p[q].d_out, r, dtype).total);
     return total;
 }
 

@@ -307,8 +307,7 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
 // its own share of the fragments: it sums them over the parts in the order
 // 0 .. ks-1, writes those V entries and clears those fragments in every
 // part, so the tile's combine is spread over ks workgroups instead of
-// resting on one. A second count lets the last part out return the counter
-// to zero.
+// resting on one. The counter's return to zero is described below.
 //
 // The wait ends: the parts of a tile have consecutive workgroup ids,
 // workgroups are dispatched in id order, and at most one tile straddles the
@@ -317,7 +316,12 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
 // out all the same (a corrupt counter), the part skips its share and
 // returns 0. Returns 1 (to all threads) once this workgroup's V entries are
 // stored.
-template <int R, bool kCoherent, typename AkOf, typename RM>
+// kSelfReset: a second count lets the last part out return the split
+// counter to zero. Without it (the fused kernel) the counter is left at ks
+// for the tile's last expand workgroup to reset: the expand workgroups start
+// only once every part has published, i.e. has passed its wait, and the
+// part's own departure round trip stays off the path to its V handoff.
+template <int R, bool kCoherent, bool kSelfReset, typename AkOf, typename RM>
 __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
                                 uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
@@ -400,8 +404,10 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
         store_frag(f, sum);
     }
     // every part has seen the full count once all of them have counted out
-    if (depart_last(split_counter, 2u * (uint32_t)ks, s_flag) && threadIdx.x == 0)
-        __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (kSelfReset) {
+        if (depart_last(split_counter, 2u * (uint32_t)ks, s_flag) && threadIdx.x == 0)
+            __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return 1;
 }
 
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                              min(t0 + kShrinkTileRows, M));
         if (pl.n == 0) return;
-        shrink_mfma_item<R, false>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
+        shrink_mfma_item<R, false, true>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
                                    kp, ks, ks > 1 ? counters + (size_t)t * kCounterStride : nullptr,
                                    partials, sm, &s_flag, rm);
     }
@@ -684,7 +690,8 @@ __device__ __forceinline__ void fused_item(
     // no counter. Each 64-row tile owns one cache line of counters: word 0
     // counts the shrink parts whose V entries are stored (polled by the
     // expand workgroups until it reaches ks), word 1 counts expand
-    // departures, word 2 synchronises the parts of a split shrink.
+    // departures, word 2 synchronises the parts of a split shrink (and is
+    // reset, with the others, by the tile's last expand workgroup).
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
     uint32_t *const tile_split = tile_counters + 2;
@@ -750,7 +757,7 @@ __device__ __forceinline__ void fused_item(
             gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
                                  t0, min(t0 + kShrinkTileRows, M));
             if (pl.n == 0) return;
-            if (shrink_mfma_item<R, true>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
+            if (shrink_mfma_item<R, true, false>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
                                           &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag, rm))
                 publish(&tile_arrive[t * kCounterStride]);
             return;
@@ -794,6 +801,10 @@ __device__ __forceinline__ void fused_item(
         if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {
             for (int q = 0; q < pl.n; ++q) zero_rows(Vws, pl.p[q].lo, pl.p[q].hi, R);
             reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
+            // the split counter too: its parts all passed their wait before publishing
+            if (ks > 1 && tid == 0)
+                __hip_atomic_store(&tile_split[t * kCounterStride], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -435,6 +435,10 @@ def main():
     touched = sum(w.algorithmic_bytes() for w in ws)
     R = args.replicas or max(1, min(256, -(-(1 << 30) // touched)))
     reps = build_replicas(ws, dev, R)
+    if args.path == "per_segment":  # per-segment metadata is copied to the GPU before any capture
+        for group in reps:
+            for rp in group:
+                rp.segments
     torch.cuda.synchronize()
 
     # one zero-filled workspace serves every fused call (they run in order on

@@ -77,7 +77,7 @@ enum sgmv_status {
     SGMV_ERR_ALIGN = -5,     /* X, Y or V not 16-byte aligned */
     SGMV_ERR_WORKSPACE = -6, /* workspace missing or smaller than sgmv_workspace_bytes */
     SGMV_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
-    SGMV_ERR_ADAPTER = -8    /* host metadata: a negative adapter id */
+    SGMV_ERR_ADAPTER = -8    /* host metadata: an adapter id that is negative (or outside the pool) */
 };
 
 /*
@@ -242,6 +242,21 @@ size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32
  */
 int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
                         int32_t *seg_start, int32_t *seg_adapter, int32_t *num_segments);
+
+/*
+ * Host-side check of segment metadata before it is copied to the device
+ * (the conditions the calls above state for seg_start and seg_adapter; the
+ * Punica guide, "The SGMV Mathematical Formulation": offsets s_0 .. s_N
+ * that cover the batch, one adapter per segment).
+ *
+ * seg_start    host int32[num_segments + 1]; seg_adapter host int32[num_segments].
+ * Returns SGMV_OK if seg_start[0] == 0, seg_start[num_segments] == M, the
+ * offsets never decrease, and every id lies in [0, num_adapters);
+ * SGMV_ERR_SHAPE for a bad offset (or negative sizes), SGMV_ERR_ADAPTER for
+ * an id outside the pool, SGMV_ERR_NULL for a missing array. Reads only.
+ */
+int sgmv_check_segments(const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                        int32_t M, int32_t num_adapters);
 
 /*
  * Adapter pool pointer table (Punica guide, figure "SGMV Kernel Memory

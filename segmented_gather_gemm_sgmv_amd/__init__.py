@@ -49,6 +49,7 @@ EXPORTS = {
     "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
+    "sgmv_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
     "sgmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sgmv_version": (ctypes.c_int, []),
 }
@@ -365,12 +366,52 @@ def sgmv_admit_adapter(A_slot: torch.Tensor, B_slot: torch.Tensor, A_host: torch
     _check("sgmv_admit_adapter", st)
 
 
+def sgmv_check_segments(seg_start, seg_adapter, M: int, num_adapters: int) -> None:
+    """Host check of segment metadata (numpy or CPU tensors): raises SGMVError
+    unless the offsets start at 0, end at M and never decrease, and every
+    adapter id lies in the pool."""
+    ss = np.ascontiguousarray(np.asarray(seg_start, dtype=np.int32))
+    sa = np.ascontiguousarray(np.asarray(seg_adapter, dtype=np.int32))
+    if ss.ndim != 1 or sa.ndim != 1 or ss.shape[0] != sa.shape[0] + 1:
+        raise ValueError("seg_start must hold one more entry than seg_adapter")
+    _check("sgmv_check_segments",
+           lib.sgmv_check_segments(ss.ctypes.data, sa.ctypes.data if sa.size else None, sa.shape[0], M,
+                                   num_adapters))
+
+
+class AdapterPool:
+    """One projection's adapter pool in HBM: P slots of A (r x d_in) and B
+    (r x d_out), packed back to back, with their device pointer tables.
+
+    ``A_ptrs`` / ``B_ptrs`` are what the SGMV calls take. ``admit`` copies an
+    adapter from host memory into a slot and points the slot's table entries
+    at it, in stream order (sgmv_admit_adapter); the slot's memory is this
+    pool's own."""
+
+    def __init__(self, num_adapters: int, d_in: int, d_out: int, r: int, dtype=torch.bfloat16,
+                 device="cuda"):
+        self.num_adapters, self.d_in, self.d_out, self.r, self.dtype = num_adapters, d_in, d_out, r, dtype
+        self.A = torch.zeros((num_adapters, r, d_in), dtype=dtype, device=device)
+        self.B = torch.zeros((num_adapters, r, d_out), dtype=dtype, device=device)
+        self.A_ptrs = sgmv_pool_pointers(self.A)
+        self.B_ptrs = sgmv_pool_pointers(self.B)
+
+    def admit(self, slot: int, A_host: torch.Tensor, B_host: torch.Tensor, stream=None) -> None:
+        """Adapter `slot` := (A_host, B_host), CPU tensors of shape r x d_in and
+        r x d_out (pinned for an asynchronous copy; keep them alive and
+        unchanged until the stream reaches the copy)."""
+        if not 0 <= slot < self.num_adapters:
+            raise IndexError(f"slot {slot} outside the pool of {self.num_adapters}")
+        sgmv_admit_adapter(self.A[slot], self.B[slot], A_host, B_host, self.A_ptrs, self.B_ptrs, slot, stream)
+
+
 def sgmv_version() -> int:
     return int(lib.sgmv_version())
 
 
 __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sgmv_expand_scatter",
            "sgmv_fused_gather", "sgmv_fused_layer", "sgmv_layer_workspace_bytes", "SgmvProjection",
-           "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_workspace_bytes", "sgmv_build_segments",
+           "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_check_segments", "AdapterPool",
+           "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16"]

@@ -47,7 +47,7 @@ const char *sgmv_status_string(int status) {
         case SGMV_ERR_ALIGN: return "X, Y and V must be 16-byte aligned";
         case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
         case SGMV_ERR_HIP: return "HIP runtime error at launch";
-        case SGMV_ERR_ADAPTER: return "negative adapter id";
+        case SGMV_ERR_ADAPTER: return "adapter id negative or outside the pool";
         default: return "unknown status";
     }
 }
@@ -286,6 +286,18 @@ int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const voi
     if (hipMemcpyAsync(B_slot, B_host, B_bytes, hipMemcpyHostToDevice, st) != hipSuccess) return SGMV_ERR_HIP;
     return hip_status(sgmv::launch_set_slot(A_ptrs, B_ptrs, slot, reinterpret_cast<uintptr_t>(A_slot),
                                             reinterpret_cast<uintptr_t>(B_slot), st));
+}
+
+int sgmv_check_segments(const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
+                        int32_t M, int32_t num_adapters) {
+    if (num_segments < 0 || M < 0 || num_adapters < 0) return SGMV_ERR_SHAPE;
+    if (!seg_start || (num_segments > 0 && !seg_adapter)) return SGMV_ERR_NULL;
+    if (seg_start[0] != 0 || seg_start[num_segments] != M) return SGMV_ERR_SHAPE;
+    for (int32_t s = 0; s < num_segments; ++s) {
+        if (seg_start[s + 1] < seg_start[s]) return SGMV_ERR_SHAPE;
+        if (seg_adapter[s] < 0 || seg_adapter[s] >= num_adapters) return SGMV_ERR_ADAPTER;
+    }
+    return SGMV_OK;
 }
 
 int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,

@@ -244,3 +244,26 @@ def test_admit_argument_errors():
     assert admit(slot=-1) == -2 and admit(slot=4) == -2 and admit(P=0, slot=0) == -2
     assert admit(Ab=0) == -2 and admit(Bb=0) == -2
     assert admit(A_slot=P1 + 8) == -5 and admit(B_slot=P2 + 4) == -5
+
+
+def test_check_segments():
+    ok = sg.sgmv_check_segments
+    ok([0, 1, 3, 3, 8], [2, 0, 3, 1], 8, 4)              # an empty segment is fine
+    ok([0], [], 0, 4)
+    pins.check_segments([2, 0, 3, 1], *oracle_pkg.build_segments(np.array([2, 0, 3, 1])))
+    perm, ss, sa = sg.sgmv_build_segments(np.array([5, 1, 5, 0], np.int32))
+    ok(ss, sa, 4, 6)
+    for bad_start, bad_ids, M, P, status in [
+        ([1, 3, 8], [0, 1], 8, 4, -2),       # does not start at 0
+        ([0, 3, 7], [0, 1], 8, 4, -2),       # does not end at M
+        ([0, 5, 3, 8], [0, 1, 2], 8, 4, -2),  # decreasing
+        ([0, 3, 8], [0, 4], 8, 4, -8),       # id outside the pool
+        ([0, 3, 8], [-1, 1], 8, 4, -8),      # negative id
+        ([0], [], 3, 4, -2),                 # no segment cannot cover 3 rows
+    ]:
+        with pytest.raises(sg.SGMVError) as e:
+            ok(bad_start, bad_ids, M, P)
+        assert e.value.status == status
+    assert sg.lib.sgmv_check_segments(None, None, 0, 0, 1) == -1
+    with pytest.raises(ValueError):
+        ok([0, 8], [0, 1], 8, 4)

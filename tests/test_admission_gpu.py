@@ -67,3 +67,27 @@ def test_admission_is_stream_ordered(dev, oracle, dtype):
     assert tab_B[3] == base_B and tab_B[1] == base_B + spare_B[0].numel() * spare_B.element_size()
     assert torch.equal(c.A_pool.cpu(), w.A_pool) and torch.equal(c.B_pool.cpu(), w.B_pool)
     assert torch.equal(spare_A[0].cpu(), new[3][0]) and torch.equal(spare_B[1].cpu(), new[1][1])
+
+
+def test_adapter_pool_admit_and_run(dev, oracle):
+    """AdapterPool: every slot filled by admission from pinned host memory,
+    then a fused call on its tables equals the oracle on the same weights."""
+    rng = np.random.Generator(np.random.PCG64(112))
+    w = wl.Workload("pool", 40, 512, 264, 16, 32.0, torch.bfloat16, 4,
+                    wl.segments_from_lengths([1, 17, 2, 20]), np.array([3, 0, 2, 3], np.int32))
+    wl.fill_tensors(w, rng)
+    w.Y = wl._normal(rng, (w.M, w.d_out), 1.0, w.dtype)
+    sg.sgmv_check_segments(w.seg_start, w.seg_adapter, w.M, w.num_adapters)
+    pool = sg.AdapterPool(w.num_adapters, w.d_in, w.d_out, w.r, w.dtype, device=dev)
+    hosts = [(pinned_copy(w.A_pool[k]), pinned_copy(w.B_pool[k])) for k in range(w.num_adapters)]
+    for k, (a, b) in enumerate(hosts):
+        pool.admit(k, a, b)
+    c = to_device(w, dev, A_pool=pool.A, B_pool=pool.B)
+    Y = c.Y0.clone()
+    sg.sgmv_fused(Y, c.X, pool.A_ptrs, pool.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
+    torch.cuda.synchronize()
+    _, Y_ref = oracle_run(oracle, w)
+    assert_close(Y, Y_ref, what="pool")
+    assert torch.equal(pool.A.cpu(), w.A_pool) and torch.equal(pool.B.cpu(), w.B_pool)
+    with pytest.raises(IndexError):
+        pool.admit(4, *hosts[0])

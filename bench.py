@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-hbm-probe", action="store_true",
+                   help="skip the streaming-read probe of what a plain kernel reaches")
     p.add_argument("--admission", action="store_true",
                    help="also time adapter admission from pinned host memory (7B and 70B adapters)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -320,6 +322,53 @@ def time_kernels(reps, path, steps, wsbuf):
     return out
 
 
+def hbm_probe(dev, workload_bytes):
+    """What a plain streaming-read kernel (the library's stream probe) reaches
+    on this GPU: over 4 GiB, and over the workload's own byte count (windows
+    rotated over 1 GiB, so the Infinity Cache cannot serve them), best of a
+    few grid sizes, each from a replayed HIP graph timed with events."""
+    import torch
+    import segmented_gather_gemm_sgmv_amd as sg
+    stream = torch.cuda.current_stream()
+
+    def timed(launches, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for src, n, sink in launches:
+                sg.sgmv_stream_probe(src, sink, n)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * len(launches))   # us per launch
+
+    out = {}
+    big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    best = None
+    for blocks in (256, 512, 1024, 2048, 4096):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        us = timed([(big, big.numel(), sink)], 5)
+        best = us if best is None or us < best else best
+    out["GB_per_s_4GiB"] = big.numel() / (best * 1e-6) / 1e9
+    del big
+    n = (workload_bytes + 15) // 16 * 16
+    windows = max(1, (1 << 30) // n)
+    buf = torch.empty(windows * n, dtype=torch.uint8, device=dev)
+    best, best_blocks = None, None
+    for blocks in (256, 512, 1024, 2048):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        us = timed([(buf[i * n:(i + 1) * n], n, sink) for i in range(windows)], 20)
+        if best is None or us < best:
+            best, best_blocks = us, blocks
+    out.update({"bytes_at_workload_size": n, "us_at_workload_size": best, "blocks": best_blocks,
+                "GB_per_s_at_workload_size": n / (best * 1e-6) / 1e9})
+    return out
+
+
 def admission_times(dev, reps=40):
     """sgmv_admit_adapter from pinned host memory: one adapter of each shape
     (every projection of a 7B and of a 70B layer, r = 16, bf16), copied into
@@ -523,6 +572,10 @@ def main():
                      "traffic": profiled_traffic(args.workload, args.path, dom),
                      "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
     }
+    if not args.no_hbm_probe:
+        probe = hbm_probe(dev, nbytes)
+        probe["value_over_probe_at_workload_size"] = value / probe["GB_per_s_at_workload_size"]
+        out["hbm_probe"] = probe
     if args.admission:
         out["admission"] = admission_times(dev)
     if not args.no_cpu_baseline:

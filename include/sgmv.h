@@ -294,6 +294,17 @@ int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const voi
                        size_t A_bytes, size_t B_bytes, uint64_t *A_ptrs, uint64_t *B_ptrs,
                        int32_t slot, int32_t num_adapters, void *stream);
 
+/*
+ * Measurement helper, not part of SGMV: a streaming read of `bytes` bytes at
+ * `src` (device, 16-byte aligned, bytes a multiple of 16) by `num_blocks`
+ * workgroups of 256 threads, 16-byte loads, each workgroup writing the XOR
+ * of the 32-bit words it read to sink[block] (device uint32[num_blocks]).
+ * It gives the HBM rate a plain kernel reaches for a given size, the
+ * ceiling the SGMV kernels are compared with. Returns SGMV_ERR_NULL,
+ * _SHAPE or _ALIGN on bad arguments.
+ */
+int sgmv_stream_probe(const void *src, size_t bytes, uint32_t *sink, int32_t num_blocks, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *sgmv_status_string(int status);
 

@@ -50,6 +50,7 @@ EXPORTS = {
     "sgmv_build_segments": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
     "sgmv_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
+    "sgmv_stream_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "sgmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sgmv_version": (ctypes.c_int, []),
 }
@@ -405,13 +406,25 @@ class AdapterPool:
         sgmv_admit_adapter(self.A[slot], self.B[slot], A_host, B_host, self.A_ptrs, self.B_ptrs, slot, stream)
 
 
+def sgmv_stream_probe(src: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, stream=None) -> None:
+    """Measurement helper: stream-read `nbytes` (default: all) of the device
+    tensor `src` with sink.numel() workgroups; sink (int32) receives each
+    workgroup's XOR of the words it read."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the source tensor")
+    st = lib.sgmv_stream_probe(_dev(src, "src"), n, _dev(sink, "sink", torch.int32, 1), sink.numel(),
+                               _stream(src, stream))
+    _check("sgmv_stream_probe", st)
+
+
 def sgmv_version() -> int:
     return int(lib.sgmv_version())
 
 
 __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sgmv_expand_scatter",
            "sgmv_fused_gather", "sgmv_fused_layer", "sgmv_layer_workspace_bytes", "SgmvProjection",
-           "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_check_segments", "AdapterPool",
+           "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_check_segments", "AdapterPool", "sgmv_stream_probe",
            "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16"]

@@ -288,6 +288,13 @@ int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const voi
                                             reinterpret_cast<uintptr_t>(B_slot), st));
 }
 
+int sgmv_stream_probe(const void *src, size_t bytes, uint32_t *sink, int32_t num_blocks, void *stream) {
+    if (!src || !sink) return SGMV_ERR_NULL;
+    if (num_blocks <= 0 || bytes == 0 || (bytes & 15) != 0) return SGMV_ERR_SHAPE;
+    if (!aligned16(src)) return SGMV_ERR_ALIGN;
+    return hip_status(sgmv::launch_stream_probe(src, bytes / 16, sink, num_blocks, static_cast<hipStream_t>(stream)));
+}
+
 int sgmv_check_segments(const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
                         int32_t M, int32_t num_adapters) {
     if (num_segments < 0 || M < 0 || num_adapters < 0) return SGMV_ERR_SHAPE;

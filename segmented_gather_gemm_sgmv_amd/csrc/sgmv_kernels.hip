@@ -1018,6 +1018,44 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
     SGMV_RANK_SWITCH(launch_fused_t, bf16_t, a, st)
 }
 
+// Streaming read of `vecs` 16-byte vectors: the plain-kernel HBM ceiling the
+// SGMV kernels are measured against. Four loads in flight per lane per
+// step; the XOR of everything read goes to sink[block] so no load is dead.
+__global__ __launch_bounds__(kBlock) void stream_probe_kernel(const uint4 *__restrict__ src, size_t vecs,
+                                                             uint32_t *__restrict__ sink) {
+    constexpr int U = 4;
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    uint32_t acc = 0;
+    size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    for (; i + (U - 1) * stride < vecs; i += U * stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = ld16_stream(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < vecs; i += stride) {
+        const uint4 v = ld16_stream(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t part[kWavesPerBlock];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) t ^= part[w];
+        sink[blockIdx.x] = t;
+    }
+}
+
+hipError_t launch_stream_probe(const void *src, size_t vecs, uint32_t *sink, int num_blocks, hipStream_t st) {
+    hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)num_blocks), dim3(kBlock), 0, st,
+                       static_cast<const uint4 *>(src), vecs, sink);
+    return hipGetLastError();
+}
+
 // One pool slot's table entries, written by one lane (vector stores).
 __global__ __launch_bounds__(kWave) void set_slot_kernel(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot,
                                                         uint64_t a, uint64_t b) {

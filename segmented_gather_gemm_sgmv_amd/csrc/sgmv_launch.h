@@ -184,6 +184,7 @@ hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs &a, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t stream);
 hipError_t launch_fused_layer(const LayerCall &a, hipStream_t stream);
+hipError_t launch_stream_probe(const void *src, size_t vecs, uint32_t *sink, int num_blocks, hipStream_t stream);
 hipError_t launch_set_slot(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot, uint64_t a, uint64_t b,
                            hipStream_t stream);
 

@@ -557,3 +557,64 @@ def test_large_batch(dev, oracle):
     sg.sgmv_fused_gather(Yg, Xg, rows_t, c.A_ptrs, c.B_ptrs, c.seg_start, c.seg_adapter, w.r, w.alpha)
     torch.cuda.synchronize()
     assert_close(Yg[rows_t.long()][r_t], Y_ref, what="fused_gather Y")
+
+
+def test_graph_replays_gathered_and_layer(dev, oracle):
+    """The gathered calls and the layer call captured in HIP graphs and
+    replayed, with eager work in between: every replay bitwise equal to the
+    oracle (integer inputs), the workspace left zero."""
+    rng = np.random.Generator(np.random.PCG64(96))
+    lengths = [1, 9, 130, 1, 3, 70, 15, 1]
+    ids = rng.integers(0, 6, size=len(lengths)).astype(np.int32)
+    ws_ = []
+    for d_in, d_out in ((1024, 520), (520, 1024)):
+        w = wl.Workload("graph", int(sum(lengths)), d_in, d_out, 16, 32.0, torch.bfloat16, 6,
+                        wl.segments_from_lengths(lengths), ids)
+        wl.fill_tensors(w, rng)
+        ws_.append(wl.integer_case(rng, w))
+    rows = rng.permutation(ws_[0].M).astype(np.int32)
+    cs = [to_device(w, dev) for w in ws_]
+    rt = torch.from_numpy(rows).to(dev)
+    want_g = [oracle_bits(oracle, orc_y, w.dtype) for w, orc_y in
+              ((w, oracle.sgmv_gather(wl.storage(w.Y), wl.storage(w.X), wl.storage(w.A_pool),
+                                      wl.storage(w.B_pool), w.seg_start, w.seg_adapter, rows, w.alpha))
+               for w in ws_)]
+    want = [oracle_bits(oracle, oracle_run(oracle, w)[1], w.dtype) for w in ws_]
+    need = max(sg.sgmv_layer_workspace_bytes([(c.Y0, c.X, c.A_ptrs, c.B_ptrs) for c in cs],
+                                             ws_[0].num_segments, ws_[0].M, 16, torch.bfloat16),
+               sg.sgmv_workspace_bytes(ws_[0].num_segments, ws_[0].M, 1024, 1024, 16, torch.bfloat16))
+    WS = torch.zeros(need, dtype=torch.uint8, device=dev)
+    Ys = [torch.empty_like(c.Y0) for c in cs]
+    V = torch.empty((ws_[0].M, 16), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    graphs = {}
+    for name in ("fused_gather", "split_gather", "layer"):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for Y, c in zip(Ys, cs):
+                Y.copy_(c.Y0)
+            c0 = cs[0]
+            if name == "fused_gather":
+                sg.sgmv_fused_gather(Ys[0], c0.X, rt, c0.A_ptrs, c0.B_ptrs, c0.seg_start, c0.seg_adapter, 16,
+                                     32.0, workspace_buf=WS)
+            elif name == "split_gather":
+                sg.sgmv_shrink_gather(V, c0.X, rt, c0.A_ptrs, c0.seg_start, c0.seg_adapter, 16, workspace_buf=WS)
+                sg.sgmv_expand_scatter(Ys[0], V, rt, c0.B_ptrs, c0.seg_start, c0.seg_adapter, 16, 32.0)
+            else:
+                sg.sgmv_fused_layer([(Y, c.X, c.A_ptrs, c.B_ptrs) for Y, c in zip(Ys, cs)], c0.seg_start,
+                                    c0.seg_adapter, 16, 32.0, workspace_buf=WS)
+        graphs[name] = g
+    for rep in range(4):
+        for name, g in graphs.items():
+            for Y in Ys:
+                Y.fill_(0)  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if name == "layer":
+                for q in range(2):
+                    assert np.array_equal(bits(Ys[q]), want[q]), (name, q, rep)
+            else:
+                assert np.array_equal(bits(Ys[0]), want_g[0]), (name, rep)
+            assert int(torch.count_nonzero(WS)) == 0, (name, rep)

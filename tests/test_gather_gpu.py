@@ -114,7 +114,7 @@ def test_gather_indexing_signature(dev, name, mode):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("r", [8, 16, 64])
+@pytest.mark.parametrize("r", [8, 16, 32, 64])
 def test_gather_random_small(dev, oracle, dtype, r):
     """Ragged segments (empty ones and ones of 16+ rows), random token order."""
     rng = np.random.Generator(np.random.PCG64(92 + r + (dtype == torch.float32)))

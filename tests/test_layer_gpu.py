@@ -58,9 +58,10 @@ SHAPES = [(1024, 1024), (1024, 136), (264, 2048), (2048, 1024)]
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("gathered", [False, True])
-def test_layer_matches_oracle_and_single_calls(dev, oracle, dtype, gathered):
-    rng = np.random.Generator(np.random.PCG64(100 + gathered + 2 * (dtype == torch.float32)))
-    ws = layer_case(rng, dtype, [3, 70, 1, 0, 130, 17, 2], [4, 1, 0, 2, 3, 1, 5], 6, SHAPES)
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_layer_matches_oracle_and_single_calls(dev, oracle, dtype, gathered, r):
+    rng = np.random.Generator(np.random.PCG64(100 + gathered + 2 * (dtype == torch.float32) + 4 * r))
+    ws = layer_case(rng, dtype, [3, 70, 1, 0, 130, 17, 2], [4, 1, 0, 2, 3, 1, 5], 6, SHAPES, r=r)
     cs = [to_device(w, dev) for w in ws]
     rows = rng.permutation(ws[0].M).astype(np.int32) if gathered else None
     rt = rows_tensor(rows, dev) if gathered else None

@@ -30,12 +30,13 @@
 //    workgroups only through device-scope (agent) atomic stores and loads,
 //    performed at the device's point of coherence, so no cache writeback or
 //    invalidation is needed. On the vector path each V value travels with a
-//    ready flag in one 64-bit store and the consumer polls the values
-//    themselves. On the MFMA path each part of a shrink tile waits until its
-//    V stores have completed, then increments the tile's arrival counter,
-//    and a consumer reads V once it has seen every part. A departure counter per
-//    segment or tile lets the last consumer return V and the counters to
-//    zero, so every launch leaves the whole workspace zero.
+//    ready flag in one 64-bit store, into one copy per expand column tile;
+//    each expand workgroup polls the values of its own copy and clears them
+//    once it has read them. On the MFMA path each part of a shrink tile
+//    waits until its V stores have completed, then increments the tile's
+//    arrival counter, and a consumer reads V once it has seen every part; a
+//    departure counter per tile lets the last consumer return V and the
+//    tile's counters to zero. Every launch leaves the whole workspace zero.
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"

@@ -314,14 +314,16 @@ def test_fused_back_to_back_fresh_values(dev, oracle):
         assert np.array_equal(bits(run_fused(c, workspace=WS)), oracle_bits(oracle, Y_ref, w.dtype)), call
 
 
-@pytest.mark.parametrize("r,d_in", [(16, 4096), (64, 4096), (16, 4104), (32, 4224)])
+@pytest.mark.parametrize("r,d_in", [(16, 4096), (64, 4096), (16, 4104), (32, 4224), (64, 28672)])
 def test_few_long_rows_split_reduction(dev, oracle, r, d_in):
     """Batches with few tiles of long rows split d_in between workgroups and
     combine the parts in the workspace, in a fixed order: check the values
     that integer inputs stay bit-exact and that the workspace is left zero.
     d_in = 4104 ends in a partial
     macro step; with 4104 and 4224 (33 macro steps in 8 parts) the last part
-    has no steps at all and contributes zeros."""
+    has no steps at all and contributes zeros. d_in = 28672 with r = 64 is
+    the largest reduction of the workloads (the 70B down projection) at the
+    largest rank: integer partial sums still stay below 2^24."""
     rng = np.random.Generator(np.random.PCG64(66 + r + d_in))
     WS = torch.zeros(1 << 23, dtype=torch.uint8, device=dev)
     for lengths in ([16], [37], [1, 20, 3, 40], [64, 64], [70, 2, 150]):

@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold-calls", type=int, default=50,
+                   help="calls timed one by one after writing 1 GiB, which evicts L2 and the Infinity Cache (0: skip)")
     p.add_argument("--no-hbm-probe", action="store_true",
                    help="skip the streaming-read probe of what a plain kernel reaches")
     p.add_argument("--admission", action="store_true",
@@ -320,6 +322,28 @@ def time_kernels(reps, path, steps, wsbuf):
         out[name] = a.elapsed_time(b) * 1e3 / launches   # microseconds per launch
         del g
     return out
+
+
+def cold_calls(reps, path, wsbuf, n):
+    """Each step timed on its own, right after a 1 GiB write that evicts the
+    L2s and the 256 MB Infinity Cache: HIP events bracket the step alone, on
+    the stream it runs on (the host enqueues the step while the write runs,
+    so the events see no launch gap). Median, p10 and p90 in microseconds."""
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=reps[0][0].X.device)
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for i in range(n):
+        flush.fill_(i & 0xff)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(reps[i % len(reps)], path, wsbuf)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    return {"calls": n, "median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+            "p90_us": float(np.percentile(us, 90))}
 
 
 def hbm_probe(dev, workload_bytes):
@@ -572,6 +596,8 @@ def main():
                      "traffic": profiled_traffic(args.workload, args.path, dom),
                      "bytes_per_launch": per_kernel[dom], "us_per_launch": kus[dom]},
     }
+    if args.cold_calls > 0:
+        out["cold"] = cold_calls(reps, args.path, wsbuf, args.cold_calls)
     if not args.no_hbm_probe:
         probe = hbm_probe(dev, nbytes)
         probe["value_over_probe_at_workload_size"] = value / probe["GB_per_s_at_workload_size"]

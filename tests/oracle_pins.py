@@ -27,6 +27,11 @@ What each pin rests on:
 * scale — alpha doubled doubles the delta exactly (power-of-two scaling).
 * bf16_rounding — the oracle's rounding agrees with torch's fp32 -> bf16
   conversion, and with hand-checked ties.
+* f32_rounding — the oracle's rounding of its float64 results to binary32
+  (the expected bits of every fp32 bitwise GPU test) against values worked by
+  hand from the binary32 format: ties to even, a near-tie that a double
+  rounding would get wrong, overflow at the exact threshold, and the
+  subnormal grid.
 * segments — the grouping of tokens by adapter is a stable sort with correct
   run starts.
 * gather_per_token — with the batch left in token order, the gathered call
@@ -266,6 +271,61 @@ def pin_bf16_rounding(orc):
     assert [int(v) for v in got] == list(cases.values()), [hex(int(v)) for v in got]
 
 
+def pin_f32_rounding(orc):
+    """Binary32 keeps 24 significant bits, exponents down to 2^-126 for
+    normal numbers, subnormals on the fixed grid 2^-149, and its largest
+    finite value is (2 - 2^-23) 2^127. Rounding is to nearest, ties to even.
+    Each expected value below is worked by hand from those facts."""
+    f32_max = float(np.float32(3.4028234663852886e38))
+    assert f32_max == (2.0 - 2.0 ** -23) * 2.0 ** 127
+    cases = [
+        # 1 + 2^-24 lies halfway between 1 and 1 + 2^-23: even -> 1
+        (1 + 2.0 ** -24, 1.0),
+        # 1 + 3 2^-24 lies halfway between 1 + 2^-23 (odd) and 1 + 2^-22 (even)
+        (1 + 3 * 2.0 ** -24, 1 + 2.0 ** -22),
+        # just above the first tie: up. Rounding first to 25 bits and then to
+        # 24 (a double rounding) would make it an exact tie and give 1.0
+        (1 + 2.0 ** -24 + 2.0 ** -52, 1 + 2.0 ** -23),
+        # just below the second tie: down to 1 + 2^-23
+        (1 + 3 * 2.0 ** -24 - 2.0 ** -52, 1 + 2.0 ** -23),
+        (-(1 + 2.0 ** -24 + 2.0 ** -52), -(1 + 2.0 ** -23)),
+        # exactly representable values pass through
+        (0.0, 0.0), (1.5, 1.5), (-1234.5, -1234.5), (2.0 ** -126, 2.0 ** -126), (f32_max, f32_max),
+        # overflow: (2 - 2^-24) 2^127 is halfway between the largest finite
+        # value (odd significand) and 2^128: even -> infinity; just below it
+        # rounds to the largest finite value
+        ((2.0 - 2.0 ** -24) * 2.0 ** 127, np.inf),
+        (-(2.0 - 2.0 ** -24) * 2.0 ** 127, -np.inf),
+        ((2.0 - 2.0 ** -24 - 2.0 ** -50) * 2.0 ** 127, f32_max),
+        (1e300, np.inf), (np.inf, np.inf), (-np.inf, -np.inf),
+        # subnormals: the grid is 2^-149; 2^-150 is halfway between 0 and
+        # 2^-149 -> even (0); 3 2^-150 halfway between 2^-149 (odd) and 2^-148
+        (2.0 ** -149, 2.0 ** -149), (2.0 ** -150, 0.0), (3 * 2.0 ** -150, 2.0 ** -148),
+        (2.0 ** -150 + 2.0 ** -170, 2.0 ** -149), (5 * 2.0 ** -151, 2.0 ** -149),
+        (-(3 * 2.0 ** -150), -(2.0 ** -148)), (2.0 ** -160, 0.0),
+        # the largest subnormal and the step into the normal range
+        ((2.0 ** 23 - 1) * 2.0 ** -149, (2.0 ** 23 - 1) * 2.0 ** -149),
+        ((2.0 ** 23 - 0.5) * 2.0 ** -149, 2.0 ** -126),
+    ]
+    x = np.array([c[0] for c in cases], np.float64)
+    got = orc.round_f32(x).astype(np.float64)
+    want = np.array([c[1] for c in cases], np.float64)
+    bad = [(x[i], got[i], want[i]) for i in range(len(cases)) if not got[i] == want[i]]
+    assert not bad, bad
+    # signs of zero survive: -0.0 and a negative value that rounds to zero
+    z = orc.round_f32(np.array([-0.0, -(2.0 ** -151)]))
+    assert np.all(z == 0) and np.all(np.signbit(z))
+    assert np.isnan(orc.round_f32(np.array([np.nan]))[0])
+    # a value between two binary32 neighbours goes to the nearer one: with
+    # 24 significant bits the neighbours of 1 + t (0 < t < 2^-23) are 1 and
+    # 1 + 2^-23
+    rng = np.random.Generator(np.random.PCG64(23))
+    t = rng.uniform(0, 2.0 ** -23, size=2000)
+    t = t[np.abs(t - 2.0 ** -24) > 2.0 ** -50]
+    got = orc.round_f32(1.0 + t).astype(np.float64)
+    assert np.array_equal(got, np.where(t < 2.0 ** -24, 1.0, 1.0 + 2.0 ** -23))
+
+
 def check_segments(token_adapter, perm, seg_start, seg_adapter):
     """The defining properties of grouping tokens by adapter: perm is a
     permutation; ids along perm are non-decreasing; equal ids keep their
@@ -345,4 +405,4 @@ def pin_gather_per_token(orc, build_segments=None):
 
 ALL_PINS = [pin_dense_single_adapter, pin_dense_mask, pin_integer_bruteforce, pin_handworked,
             pin_zero_adapter, pin_linearity, pin_permutation, pin_signature, pin_scale,
-            pin_bf16_rounding, pin_gather_per_token]
+            pin_bf16_rounding, pin_f32_rounding, pin_gather_per_token]

@@ -39,6 +39,11 @@ MUTANTS = [
     ("bf16_round_7_bits", "nearbyint(ldexp(f, 8)), e - 8", "nearbyint(ldexp(f, 7)), e - 7", 0),
     ("adapter_stride", "k * (int64_t)r * d_in", "k * (int64_t)d_in", 0),
     ("V_transposed_store", "V[m * r + j] = acc;", "V[j * M + m] = acc;", 0),
+    # binary32 output rounding: truncation toward zero, and rounding to bf16 width
+    ("f32_round_truncates", "out[i] = (float)in[i];",
+     "{ float f = (float)in[i]; if (fabs((double)f) > fabs(in[i])) f = nextafterf(f, 0.0f); out[i] = f; }", 0),
+    ("f32_round_bf16_width", "out[i] = (float)in[i];",
+     "{ int e; double f = frexp(in[i], &e); out[i] = (float)ldexp(nearbyint(ldexp(f, 8)), e - 8); }", 0),
 ]
 
 

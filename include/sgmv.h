@@ -51,10 +51,20 @@
  * error nothing is enqueued. M == 0 or num_segments == 0 is a successful
  * no-op. Device-resident metadata cannot be checked without a
  * synchronisation, so the kernels defend themselves instead: segment bounds
- * are clamped into [0, M] (a non-increasing pair is an empty segment) and a
+ * are clamped into [0, M] (a decreasing pair is an empty segment) and a
  * segment whose adapter id lies outside [0, num_adapters) is skipped (its rows
  * are left as they were). Nothing outside the documented buffers is read or
- * written for any metadata values.
+ * written for any metadata values, and every kernel ends.
+ *
+ * Failures seen on the device (calls with a workspace): offsets that
+ * decrease somewhere let two segments share rows; the values of such rows
+ * are then unspecified, and the call sets SGMV_WS_BAD_OFFSETS in the
+ * workspace's status word. Workgroups that wait for one another do so for a
+ * bounded number of polls (sgmv_set_wait_limit); a wait that gives up leaves
+ * its rows unchanged and sets SGMV_WS_WAIT_TIMEOUT. Either bit means the
+ * workspace may hold leftovers: every later call on it does nothing (its
+ * outputs are left as they were) until the caller zero-fills the workspace
+ * again. sgmv_workspace_status reads the word.
  */
 #ifndef SGMV_H
 #define SGMV_H
@@ -304,6 +314,37 @@ int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const voi
  * _SHAPE or _ALIGN on bad arguments.
  */
 int sgmv_stream_probe(const void *src, size_t bytes, uint32_t *sink, int32_t num_blocks, void *stream);
+
+/*
+ * Workspace status (the sticky word at the start of every workspace, see
+ * "Failures seen on the device" above): 0 while every call on the workspace
+ * succeeded, else the OR of the bits below.
+ */
+enum sgmv_ws_status {
+    SGMV_WS_WAIT_TIMEOUT = 1, /* a bounded wait between workgroups gave up */
+    SGMV_WS_BAD_OFFSETS = 2   /* seg_start decreases somewhere */
+};
+
+/*
+ * Reads the status word of `workspace` (a workspace of sgmv_shrink,
+ * sgmv_fused, the gathered calls or sgmv_fused_layer) into *status after
+ * every call enqueued before it on `stream` has completed: it synchronises
+ * the stream. A non-zero status stays until the caller zero-fills the
+ * workspace (all of it: the failed call may have left leftovers anywhere in
+ * it). Returns SGMV_ERR_NULL, or SGMV_ERR_HIP if the copy or the
+ * synchronisation failed.
+ */
+int sgmv_workspace_status(const void *workspace, uint32_t *status, void *stream);
+
+/*
+ * Sets how many times a workgroup polls for another's result before it gives
+ * up (default 32768, several milliseconds at the least); applies to calls
+ * launched afterwards (a captured graph keeps the value it was captured
+ * with). Process-wide; returns the previous value. 0 makes every wait give
+ * up unless its result is there at the first poll: a way to test the failure
+ * path from the host.
+ */
+uint32_t sgmv_set_wait_limit(uint32_t polls);
 
 /* A static, human-readable name for a status code. */
 const char *sgmv_status_string(int status);

@@ -51,6 +51,8 @@ EXPORTS = {
     "sgmv_pool_pointers": (ctypes.c_int, [_vp, _vp, _i32, _i64]),
     "sgmv_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
     "sgmv_stream_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "sgmv_workspace_status": (ctypes.c_int, [_vp, _vp, _vp]),
+    "sgmv_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "sgmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sgmv_version": (ctypes.c_int, []),
 }
@@ -156,20 +158,58 @@ def sgmv_workspace_bytes(num_segments: int, M: int, d_in: int, d_out: int, r: in
 _workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
+def _torch_stream(device: torch.device, stream):
+    """`stream` (None, a torch stream or a raw hipStream_t handle) as a torch
+    stream object on `device`."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, (torch.cuda.Stream, torch.cuda.ExternalStream)):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def workspace(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
     """A zero-filled workspace for sgmv_shrink and sgmv_fused, cached per
     (device, stream).
 
     Every call leaves the workspace zero again when its kernel completes, so
-    one buffer serves every later call on the same stream."""
+    one buffer serves every later call on the same stream. The buffer is
+    allocated and zero-filled on that stream, so the fill is ordered before
+    the calls that use it, and the caching allocator hands a replaced buffer
+    to later work on the same stream only."""
     device = torch.device(device)
-    key = (device.index if device.index is not None else torch.cuda.current_device(),
-           _stream(torch.empty(0, device=device), stream))
+    if device.index is None:
+        device = torch.device(device.type, torch.cuda.current_device())
+    s = _torch_stream(device, stream)
+    key = (device.index, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        with torch.cuda.device(device), torch.cuda.stream(s):
+            ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def sgmv_workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """The workspace's sticky status word (0, or the OR of SGMV_WS_WAIT_TIMEOUT
+    and SGMV_WS_BAD_OFFSETS), read after the work enqueued on `stream`
+    (default: the current stream) has completed. A non-zero status stays
+    until the workspace is zero-filled again; until then every call on it is
+    a no-op."""
+    word = ctypes.c_uint32(0)
+    _check("sgmv_workspace_status", lib.sgmv_workspace_status(_dev(ws, "workspace"), ctypes.byref(word),
+                                                              _stream(ws, stream)))
+    return int(word.value)
+
+
+def sgmv_set_wait_limit(polls: int) -> int:
+    """Polls a waiting workgroup makes before it gives up, for calls launched
+    from now on (process-wide); returns the previous value."""
+    return int(lib.sgmv_set_wait_limit(int(polls)))
+
+
+SGMV_WS_WAIT_TIMEOUT = 1
+SGMV_WS_BAD_OFFSETS = 2
 
 
 def sgmv_fused(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: torch.Tensor,
@@ -427,4 +467,5 @@ __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sg
            "SGMV_MAX_PROJECTIONS", "sgmv_admit_adapter", "sgmv_check_segments", "AdapterPool", "sgmv_stream_probe",
            "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
-           "LIBRARY", "SGMV_F32", "SGMV_BF16"]
+           "LIBRARY", "SGMV_F32", "SGMV_BF16", "sgmv_workspace_status", "sgmv_set_wait_limit",
+           "SGMV_WS_WAIT_TIMEOUT", "SGMV_WS_BAD_OFFSETS"]

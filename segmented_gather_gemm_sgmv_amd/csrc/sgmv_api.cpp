@@ -10,6 +10,9 @@
 
 #include "sgmv_launch.h"
 
+static_assert(SGMV_WS_WAIT_TIMEOUT == sgmv::kStatusTimeout && SGMV_WS_BAD_OFFSETS == sgmv::kStatusBadOffsets,
+              "status bits of the header and the kernels agree");
+
 namespace {
 
 bool valid_rank(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
@@ -35,7 +38,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; 
 
 extern "C" {
 
-int sgmv_version(void) { return 200; }
+int sgmv_version(void) { return 300; }
 
 const char *sgmv_status_string(int status) {
     switch (status) {
@@ -294,6 +297,18 @@ int sgmv_stream_probe(const void *src, size_t bytes, uint32_t *sink, int32_t num
     if (!aligned16(src)) return SGMV_ERR_ALIGN;
     return hip_status(sgmv::launch_stream_probe(src, bytes / 16, sink, num_blocks, static_cast<hipStream_t>(stream)));
 }
+
+int sgmv_workspace_status(const void *workspace, uint32_t *status, void *stream) {
+    if (!workspace || !status) return SGMV_ERR_NULL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, st) != hipSuccess) return SGMV_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return SGMV_ERR_HIP;
+    *status = word;
+    return SGMV_OK;
+}
+
+uint32_t sgmv_set_wait_limit(uint32_t polls) { return sgmv::set_wait_limit(polls); }
 
 int sgmv_check_segments(const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
                         int32_t M, int32_t num_adapters) {

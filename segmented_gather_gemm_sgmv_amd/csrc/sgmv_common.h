@@ -191,14 +191,18 @@ struct RowMap {
 };
 
 // Segment bounds clamped into [0, M]; an inverted pair is an empty segment.
-__device__ __forceinline__ void segment_rows(const int32_t *seg_start, int s, int M, int &lo,
+// Returns whether the offsets as given decrease here (seg_start[s] >
+// seg_start[s + 1]): offsets that are not non-decreasing always do so at
+// some segment, and only then can two segments share rows.
+__device__ __forceinline__ bool segment_rows(const int32_t *seg_start, int s, int M, int &lo,
                                              int &hi) {
-    int a = seg_start[s];
-    int b = seg_start[s + 1];
-    a = a < 0 ? 0 : (a > M ? M : a);
-    b = b < 0 ? 0 : (b > M ? M : b);
+    const int a0 = seg_start[s];
+    const int b0 = seg_start[s + 1];
+    const int a = a0 < 0 ? 0 : (a0 > M ? M : a0);
+    const int b = b0 < 0 ? 0 : (b0 > M ? M : b0);
     lo = a;
     hi = b < a ? a : b;
+    return a0 > b0;
 }
 
 // Sum of NV values per lane across the 64 lanes of a wave, by recursive

@@ -38,6 +38,8 @@
 //    departure counter per tile lets the last consumer return V and the
 //    tile's counters to zero. Every launch leaves the whole workspace zero.
 
+#include <atomic>
+
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
 #include "sgmv_mfma.h"
@@ -81,14 +83,36 @@ __device__ __forceinline__ void store_v_flagged(float *V, size_t idx, float v) {
     __hip_atomic_store(reinterpret_cast<uint64_t *>(V) + idx, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr uint32_t kSpinLimit = 1u << 26;  // polls before a wait gives up (corrupt workspace)
+// The workspace's sticky status word (NULL when the call has no workspace).
+__device__ __forceinline__ uint32_t read_status(const WaitCtl &wc) {
+    return wc.status ? __hip_atomic_load(wc.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+}
+
+// Sets a status bit (call from one lane).
+__device__ __forceinline__ void report(const WaitCtl &wc, uint32_t bit) {
+    if (wc.status) __hip_atomic_fetch_or(wc.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After unsuccessful poll number `spins` (0-based, uniform): whether the wait
+// ends. It ends once `limit` polls have failed (reported as a timeout), or
+// early when another wait has already failed: every 32nd poll rereads the
+// status, so one failed wait does not leave the rest to run to their bounds.
+// `lead`: this lane reports.
+__device__ __forceinline__ bool give_up(const WaitCtl &wc, uint32_t spins, bool lead) {
+    if (spins >= wc.limit) {
+        if (lead) report(wc, kStatusTimeout);
+        return true;
+    }
+    if ((spins & 31) == 31) return __builtin_amdgcn_readfirstlane((int)read_status(wc)) != 0;
+    return false;
+}
 
 // Wave-wide: lane t < RB * JC fetches V[row0 + min(t / JC, nrows - 1)][jc + t % JC]
 // from flagged pairs, polling until every one carries its flag. Returns false
-// if the bound ran out (then `out` is meaningless).
+// if the wait gave up (then `out` is meaningless).
 template <int RB, int JC>
 __device__ __forceinline__ bool poll_v_block(const float *V, int row0, int nrows, int R, int jc,
-                                             float &out) {
+                                             float &out, const WaitCtl &wc) {
     static_assert(RB * JC <= kWave, "one pair per lane");
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane < RB * JC ? lane : 0;
@@ -100,7 +124,7 @@ __device__ __forceinline__ bool poll_v_block(const float *V, int row0, int nrows
             out = __uint_as_float((uint32_t)w);
             return true;
         }
-        if (spins > kSpinLimit) return false;
+        if (give_up(wc, spins, lane == 0)) return false;
         __builtin_amdgcn_s_sleep(2);
     }
 }
@@ -221,17 +245,23 @@ __device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_ad
 // One vector-path shrink item: rank row j of segment s, one wave. Returns
 // false if the segment is empty, names no valid adapter or belongs to the
 // MFMA path (then nothing is written).
+// The workspace status is read with the metadata: a non-zero status (an
+// earlier failure) makes the item a no-op. Offsets that decrease at this
+// segment (so that other segments may overlap) are reported, once.
 template <typename T, int R, bool kFlagged, bool kSpec, typename RM>
 __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int j, int M,
-                                                   int d_in, int lane, RM rm, int copies = 1) {
+                                                   int d_in, int lane, RM rm, const WaitCtl &wc,
+                                                   int copies = 1) {
     AdapterTable<kSpec> tab;
     tab.load(A_ptrs, num_adapters, lane);
     int lo, hi;
+    const uint32_t st = read_status(wc);
     const int k = seg_adapter[s];
-    segment_rows(seg_start, s, M, lo, hi);
-    if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
+    const bool inverted = segment_rows(seg_start, s, M, lo, hi);
+    if (inverted && j == 0 && lane == 0) report(wc, kStatusBadOffsets);
+    if (!vector_segment<T>(lo, hi, k, num_adapters) | (st != 0)) return false;
     auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
     shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane, rm, copies, (size_t)M * R);
     return true;
@@ -242,17 +272,18 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
 // the counted workgroups stored before counting themselves in (device-scope
 // atomics on both sides, see the top of the file). Each caller explains why
 // the workgroups it waits for are dispatched; the bound only guards against
-// a workspace whose counters were not zero on entry.
-__device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag) {
+// a workspace whose counters were not zero on entry or invalid metadata, and
+// a wait that gives up is reported in the status word.
+__device__ __forceinline__ int wait_for(uint32_t *counter, uint32_t target, int *s_flag, const WaitCtl &wc) {
     if (threadIdx.x == 0) {
-        uint32_t spins = 0;
         int ok = 1;
-        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(4);  // about 256 clocks between polls
-            if (++spins > (1u << 26)) {
+        for (uint32_t spins = 0;
+             __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spins) {
+            if (give_up(wc, spins, true)) {
                 ok = 0;
                 break;
             }
+            __builtin_amdgcn_s_sleep(4);  // about 256 clocks between polls
         }
         *s_flag = ok;
     }
@@ -326,7 +357,7 @@ template <int R, bool kCoherent, bool kSelfReset, typename AkOf, typename RM>
 __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
                                 uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
-                                int *s_flag, RM rm) {
+                                int *s_flag, RM rm, const WaitCtl &wc) {
     constexpr int NB = ShrinkSmem<R>::kNB;
     constexpr int kFrags = kWavesPerBlock * NB * kWave;  // 16-byte fragments per partial tile
     constexpr uint32_t kTileBytes = kFrags * 16;
@@ -382,7 +413,7 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
     for (int b = 0; b < NB; ++b)
         store4_coherent(rs, (uint32_t)kp * kTileBytes + (uint32_t)((wave * NB + b) * kWave + lane) * 16, res[b]);
     publish(split_counter);
-    if (!wait_for(split_counter, (uint32_t)ks, s_flag)) return 0;
+    if (!wait_for(split_counter, (uint32_t)ks, s_flag, wc)) return 0;
     // This part's share: fragments [f0, f1), one per thread at most while
     // kFrags / ks <= kBlock. Every part of a fragment is requested before it
     // is summed or cleared: a load placed after a store to the same buffer
@@ -449,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
     const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int ks,
-    uint32_t *counters, float *partials, RowMap<kGather> rm) {
+    uint32_t *counters, float *partials, RowMap<kGather> rm, WaitCtl wc) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = round_up_xcds(num_segments) * groups;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -460,10 +491,10 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         const int lane = threadIdx.x & (kWave - 1);
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, false, true>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, lane, rm);
+                                                  s, j, M, d_in, lane, rm, wc);
         else
             shrink_vector_item<T, R, false, false>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                   s, j, M, d_in, lane, rm);
+                                                   s, j, M, d_in, lane, rm, wc);
         return;
     }
     if constexpr (Elem<T>::kMfma) {
@@ -477,13 +508,14 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         const int t = ((int)blockIdx.x - gemv_items) / ks, kp = ((int)blockIdx.x - gemv_items) % ks;
         if (t >= tiles) return;
         const int t0 = t * kShrinkTileRows;
+        const uint32_t st = read_status(wc);
         const MfmaAdapters ak_of(A_ptrs, num_adapters);
         gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                              min(t0 + kShrinkTileRows, M));
-        if (pl.n == 0) return;
+        if (pl.n == 0 || st != 0) return;
         shrink_mfma_item<R, false, true>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
                                    kp, ks, ks > 1 ? counters + (size_t)t * kCounterStride : nullptr,
-                                   partials, sm, &s_flag, rm);
+                                   partials, sm, &s_flag, rm, wc);
     }
 }
 
@@ -493,7 +525,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
 template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready, typename RM>
 __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
                                             int nrows, int n0, bool active, float scale, Ready ready,
-                                            RM rm) {
+                                            RM rm, const WaitCtl &wc) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     // Loads are unconditional (see shrink_wave): an inactive lane reads
@@ -522,7 +554,7 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
         if (!ready()) return;  // uniform: V may be read from here on
         float vl = 0.f;  // flagged V: this lane's value of the block
         if constexpr (kFlagged) {
-            if (!poll_v_block<RB, JC>(V, row0, nrows, R, jc, vl)) return;  // wave-uniform
+            if (!poll_v_block<RB, JC>(V, row0, nrows, R, jc, vl, wc)) return;  // wave-uniform
         }
 #pragma unroll
         for (int m = 0; m < RB; ++m) {
@@ -574,38 +606,39 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
 template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready, typename RM>
 __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn, int d_out, int lo,
                                                int hi, int n0, bool active, float scale, Ready ready,
-                                               RM rm) {
+                                               RM rm, const WaitCtl &wc) {
     static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
     for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
         const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
+            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
+            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
         else if (kMaxRB == 4 || nrows <= 4)
-            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
+            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
         else if constexpr (kMaxRB == 8)
-            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm);
+            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
     }
 }
 
 // One vector-path expand item: columns n0 .. n0 + VEC - 1 (per thread) of
 // segment s; `ready` as for expand_segment. Returns false if the segment is
-// empty, names no valid adapter or belongs to the MFMA path. lo, hi receive
-// the segment's rows.
+// empty, names no valid adapter, belongs to the MFMA path or the workspace
+// status is not zero. lo, hi receive the segment's rows.
 template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn, typename RM>
 __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int n0, int M,
                                                    int d_out, float scale, int &lo, int &hi,
-                                                   ReadyFn ready, RM rm) {
+                                                   ReadyFn ready, RM rm, const WaitCtl &wc) {
     AdapterTable<kSpec> tab;
     tab.load(B_ptrs, num_adapters, threadIdx.x & (kWave - 1));
+    const uint32_t st = read_status(wc);
     const int k = seg_adapter[s];
     segment_rows(seg_start, s, M, lo, hi);
-    if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
+    if (!vector_segment<T>(lo, hi, k, num_adapters) | (st != 0)) return false;
     auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
-    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm);
+    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm, wc);
     return true;
 }
 
@@ -631,7 +664,8 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         // B_k's address is loaded once the id is known: reading the table
         // early measured slower here, where Y is requested alongside B
         expand_vector_item<T, R, false, kMaxRB, false>(Y, V, B_ptrs, num_adapters, seg_start, seg_adapter,
-                                                       s, n0, M, d_out, scale, lo, hi, []() { return true; }, rm);
+                                                       s, n0, M, d_out, scale, lo, hi, []() { return true; }, rm,
+                                                       WaitCtl{nullptr, 0});
         return;
     }
     if constexpr (Elem<T>::kMfma) {
@@ -685,7 +719,7 @@ __device__ __forceinline__ void fused_item(
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
     int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials, RowMap<kGather> rm, const int item) {
+    float *Vpairs, float *partials, RowMap<kGather> rm, const WaitCtl &wc, const int item) {
     // The vector path hands V over as flagged pairs (Vpairs), one copy per
     // expand column tile, so each expand workgroup clears its own copy with
     // no counter. Each 64-row tile owns one cache line of counters: word 0
@@ -711,10 +745,10 @@ __device__ __forceinline__ void fused_item(
         const int j = grp * kWavesPerBlock + tid / kWave;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                 s, j, M, d_in, tid & (kWave - 1), rm, ntiles_g);
+                                                 s, j, M, d_in, tid & (kWave - 1), rm, wc, ntiles_g);
         else
             shrink_vector_item<T, R, true, false>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, tid & (kWave - 1), rm, ntiles_g);
+                                                  s, j, M, d_in, tid & (kWave - 1), rm, wc, ntiles_g);
         return;
     }
     if (item >= a1 && item < a2) {
@@ -731,10 +765,10 @@ __device__ __forceinline__ void fused_item(
             num_adapters <= kSpecTable
                 ? expand_vector_item<T, R, true, kFusedRB, true>(Y, Vcopy, B_ptrs, num_adapters, seg_start,
                                                                  seg_adapter, s, n0, M, d_out, scale,
-                                                                 lo, hi, ready, rm)
+                                                                 lo, hi, ready, rm, wc)
                 : expand_vector_item<T, R, true, kFusedRB, false>(Y, Vcopy, B_ptrs, num_adapters, seg_start,
                                                                   seg_adapter, s, n0, M, d_out, scale,
-                                                                  lo, hi, ready, rm);
+                                                                  lo, hi, ready, rm, wc);
         if (!valid) return;
         // every wave of this workgroup has read its values: clear the copy
         // (no other workgroup reads it)
@@ -754,12 +788,13 @@ __device__ __forceinline__ void fused_item(
             // the tile's V on the tile's arrival word
             const int t = (item - a0) / ks, kp = (item - a0) % ks;
             const int t0 = t * kShrinkTileRows;
+            const uint32_t st = read_status(wc);
             const MfmaAdapters ak_of(A_ptrs, num_adapters);
             gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
                                  t0, min(t0 + kShrinkTileRows, M));
-            if (pl.n == 0) return;
+            if (pl.n == 0 || st != 0) return;
             if (shrink_mfma_item<R, true, false>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
-                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag, rm))
+                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag, rm, wc))
                 publish(&tile_arrive[t * kCounterStride]);
             return;
         }
@@ -769,11 +804,14 @@ __device__ __forceinline__ void fused_item(
         const int t0 = t * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
         const int n0 = (e % ntiles_m) * kExpandTileCols;
+        const uint32_t st = read_status(wc);
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
-        // the shrink tile with the same rows is done once all its parts report
+        // the shrink tile with the same rows is done once all its parts report;
+        // a non-zero status on entry makes the tile a no-op
         int state = -1;  // uniform: -1 not yet waited, else the result of the wait
         auto ready = [&]() {
-            if (state < 0) state = wait_for(&tile_arrive[t * kCounterStride], (uint32_t)ks, &s_flag);
+            if (state < 0)
+                state = st == 0 && wait_for(&tile_arrive[t * kCounterStride], (uint32_t)ks, &s_flag, wc);
             return state != 0;
         };
         // V of this tile's rows, read at device scope (written in this launch)
@@ -817,10 +855,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
     int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials, RowMap<kGather> rm) {
+    float *Vpairs, float *partials, RowMap<kGather> rm, WaitCtl wc) {
     fused_item<T, R, kGather>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
                               d_in, d_out, ntiles_g, ntiles_m, num_tiles, ks, scale, long_batch,
-                              tile_counters, Vws, Vpairs, partials, rm, (int)blockIdx.x);
+                              tile_counters, Vws, Vpairs, partials, rm, wc, (int)blockIdx.x);
 }
 
 // Layer-batched fused launch (the launch accounting of the Punica guide's
@@ -844,7 +882,7 @@ __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
     fused_item<T, R, kGather>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
                               d.B_ptrs, d.num_adapters, seg_start, seg_adapter, num_segments, M, d.d_in,
                               d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.ks, scale, long_batch,
-                              d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, item);
+                              d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, L.wc, item);
 }
 
 // ----------------------------------------------------------------------------
@@ -874,7 +912,8 @@ static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
                        a.seg_adapter, a.num_segments, a.M, a.d_in, L.ks,
                        L.ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
                        L.ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr,
-                       RowMap<kGather>{a.rows, a.M});
+                       RowMap<kGather>{a.rows, a.M},
+                       WaitCtl{L.total > 0 ? reinterpret_cast<uint32_t *>(ws) : nullptr, wait_limit()});
     return hipGetLastError();
 }
 
@@ -928,7 +967,8 @@ static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
                        a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, L.ks, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), tile_c,
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
-                       reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M});
+                       reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M},
+                       WaitCtl{reinterpret_cast<uint32_t *>(ws), wait_limit()});
     return hipGetLastError();
 }
 
@@ -942,6 +982,7 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
     LayerArgs L{};
     L.num_projections = a.num_projections;
     char *ws = static_cast<char *>(a.workspace);
+    L.wc = WaitCtl{reinterpret_cast<uint32_t *>(ws), wait_limit()};
     size_t ws_off = 0;
     int base = 0;
     for (int q = 0; q < a.num_projections; ++q) {
@@ -983,15 +1024,6 @@ static hipError_t launch_fused_layer_t(const LayerCall &a, hipStream_t st) {
     return a.rows ? launch_fused_layer_g<T, R, true>(a, st) : launch_fused_layer_g<T, R, false>(a, st);
 }
 
-#define SGMV_RANK_SWITCH(FN, T, args, st)           \
-    switch ((args).r) {                             \
-        case 8: return FN<T, 8>((args), (st));      \
-        case 16: return FN<T, 16>((args), (st));    \
-        case 32: return FN<T, 32>((args), (st));    \
-        case 64: return FN<T, 64>((args), (st));    \
-        default: return hipErrorInvalidValue;       \
-    }
-
 // Whether a bf16 batch can hold a segment long enough for the MFMA path:
 // with every segment non-empty, the longest has M - N + 1 rows. Batches of
 // decode tokens (one or a few rows per segment) cannot, and take kernels
@@ -1001,23 +1033,62 @@ static bool long_segments_possible(int M, int num_segments) {
     return (int64_t)M - num_segments + 1 >= kLongRows;
 }
 
-hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t st) {
-    if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_shrink_t, float, a, st)
-    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_shrink_t, bf16_short_t, a, st)
-    SGMV_RANK_SWITCH(launch_shrink_t, bf16_t, a, st)
+#ifdef SGMV_RANK
+// One rank's entry points: this file is compiled once per rank (with
+// -DSGMV_RANK=8, 16, 32, 64), so the rank's kernels build in parallel with
+// the others'.
+template <>
+hipError_t launch_shrink_rank<SGMV_RANK>(const ShrinkArgs &a, hipStream_t st) {
+    if (a.dtype == kF32) return launch_shrink_t<float, SGMV_RANK>(a, st);
+    if (!long_segments_possible(a.M, a.num_segments)) return launch_shrink_t<bf16_short_t, SGMV_RANK>(a, st);
+    return launch_shrink_t<bf16_t, SGMV_RANK>(a, st);
 }
 
-hipError_t launch_expand(const ExpandArgs &a, hipStream_t st) {
-    if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_expand_t, float, a, st)
-    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_expand_t, bf16_short_t, a, st)
-    SGMV_RANK_SWITCH(launch_expand_t, bf16_t, a, st)
+template <>
+hipError_t launch_expand_rank<SGMV_RANK>(const ExpandArgs &a, hipStream_t st) {
+    if (a.dtype == kF32) return launch_expand_t<float, SGMV_RANK>(a, st);
+    if (!long_segments_possible(a.M, a.num_segments)) return launch_expand_t<bf16_short_t, SGMV_RANK>(a, st);
+    return launch_expand_t<bf16_t, SGMV_RANK>(a, st);
 }
 
-hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
-    if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_t, float, a, st)
-    if (!long_segments_possible(a.M, a.num_segments)) SGMV_RANK_SWITCH(launch_fused_t, bf16_short_t, a, st)
-    SGMV_RANK_SWITCH(launch_fused_t, bf16_t, a, st)
+template <>
+hipError_t launch_fused_rank<SGMV_RANK>(const FusedArgs &a, hipStream_t st) {
+    if (a.dtype == kF32) return launch_fused_t<float, SGMV_RANK>(a, st);
+    if (!long_segments_possible(a.M, a.num_segments)) return launch_fused_t<bf16_short_t, SGMV_RANK>(a, st);
+    return launch_fused_t<bf16_t, SGMV_RANK>(a, st);
 }
+
+template <>
+hipError_t launch_fused_layer_rank<SGMV_RANK>(const LayerCall &a, hipStream_t st) {
+    if (a.dtype == kF32) return launch_fused_layer_t<float, SGMV_RANK>(a, st);
+    if (!long_segments_possible(a.M, a.num_segments))
+        return launch_fused_layer_t<bf16_short_t, SGMV_RANK>(a, st);
+    return launch_fused_layer_t<bf16_t, SGMV_RANK>(a, st);
+}
+
+#else  // the rank dispatch, the helper kernels and the process-wide settings
+
+#define SGMV_RANK_SWITCH(FN, args, st)               \
+    switch ((args).r) {                             \
+        case 8: return FN<8>((args), (st));         \
+        case 16: return FN<16>((args), (st));       \
+        case 32: return FN<32>((args), (st));       \
+        case 64: return FN<64>((args), (st));       \
+        default: return hipErrorInvalidValue;       \
+    }
+
+hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t st) { SGMV_RANK_SWITCH(launch_shrink_rank, a, st) }
+hipError_t launch_expand(const ExpandArgs &a, hipStream_t st) { SGMV_RANK_SWITCH(launch_expand_rank, a, st) }
+hipError_t launch_fused(const FusedArgs &a, hipStream_t st) { SGMV_RANK_SWITCH(launch_fused_rank, a, st) }
+hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
+    SGMV_RANK_SWITCH(launch_fused_layer_rank, a, st)
+}
+
+// How many polls a bounded wait makes before it gives up; read at each launch.
+static std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
+
+uint32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+uint32_t set_wait_limit(uint32_t polls) { return g_wait_limit.exchange(polls, std::memory_order_relaxed); }
 
 // Streaming read of `vecs` 16-byte vectors: the plain-kernel HBM ceiling the
 // SGMV kernels are measured against. Four loads in flight per lane per
@@ -1072,11 +1143,6 @@ hipError_t launch_set_slot(uint64_t *A_ptrs, uint64_t *B_ptrs, int slot, uint64_
     return hipGetLastError();
 }
 
-hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
-    if (a.dtype == kF32) SGMV_RANK_SWITCH(launch_fused_layer_t, float, a, st)
-    if (!long_segments_possible(a.M, a.num_segments))
-        SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_short_t, a, st)
-    SGMV_RANK_SWITCH(launch_fused_layer_t, bf16_t, a, st)
-}
+#endif  // SGMV_RANK
 
 }  // namespace sgmv

@@ -55,6 +55,25 @@ constexpr int kMacroSteps = 128;   // d_in elements per MFMA shrink macro step
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Every workspace starts with one 256-byte header line. Word 0 is the sticky
+// status of the calls that use the workspace (bits of enum sgmv_ws_status in
+// sgmv.h); the rest of the line is reserved and stays zero.
+constexpr size_t kHeaderBytes = 256;
+
+// Bounded waits: how many times a waiting workgroup polls before it gives
+// up, and where it reports that it did. `status` is NULL for a call without
+// a workspace (such a call has no cross-workgroup wait). A workgroup that
+// finds the status non-zero when it starts does nothing.
+struct WaitCtl {
+    uint32_t *status;
+    uint32_t limit;
+};
+constexpr uint32_t kDefaultWaitLimit = 1u << 15;
+constexpr uint32_t kStatusTimeout = 1;      // a bounded wait gave up
+constexpr uint32_t kStatusBadOffsets = 2;   // seg_start decreases somewhere
+uint32_t wait_limit();
+uint32_t set_wait_limit(uint32_t polls);
+
 constexpr int kCounterStride = 32;  // uint32 words per counter line (128 bytes)
 
 // How many workgroups split d_in for each 64-row MFMA shrink tile: enough for
@@ -72,8 +91,8 @@ inline int shrink_ksplit(int M, int d_in) {
     return std::max(ks, 1);
 }
 
-// Shrink workspace (bf16 only, when the split is more than one part): one
-// 128-byte counter line per 64-row tile (its parts arrived, then departed),
+// Shrink workspace (bf16 only, when the split is more than one part): the
+// header line, then one 128-byte counter line per 64-row tile (its parts arrived, then departed),
 // then the tiles' partial results (tile x part x 64 x max(r, 16) fp32: the
 // MFMA tile is at least 16 columns wide). Every launch leaves it all zero.
 struct ShrinkLayout {
@@ -85,8 +104,8 @@ inline ShrinkLayout shrink_layout(int M, int d_in, int r, int dtype) {
     ShrinkLayout L;
     L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
-    L.counters = 0;
-    L.partials = align256(kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
+    L.counters = kHeaderBytes;
+    L.partials = align256(L.counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
     L.total = L.ks > 1 ? align256(L.partials + sizeof(float) * (size_t)L.tiles * L.ks *
                                                    kTileRows64 * (size_t)std::max(r, 16))
                        : 0;
@@ -100,7 +119,8 @@ inline int vector_col_tiles(int d_out, int dtype) {
     return (d_out + cols - 1) / cols;
 }
 
-// Fused workspace: one 128-byte line of counters per 64-row tile (V
+// Fused workspace: the header line, then one 128-byte line of counters per
+// 64-row tile (V
 // complete, expand workgroups departed, split shrink parts arrived), so
 // that consumers polling one tile do not contend with another's; then V of
 // the MFMA path (M x r fp32), the split partials as above, and V of the
@@ -117,8 +137,8 @@ inline FusedLayout fused_layout(int M, int d_in, int d_out, int r, int dtype) {
     L.tiles = dtype == kBF16 ? (M + kTileRows64 - 1) / kTileRows64 : 0;
     L.ks = dtype == kBF16 ? shrink_ksplit(M, d_in) : 1;
     L.copies = vector_col_tiles(d_out, dtype);
-    L.tile_counters = 0;
-    L.v = align256(kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
+    L.tile_counters = kHeaderBytes;
+    L.v = align256(L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);
     L.partials = align256(L.v + sizeof(float) * (size_t)M * (size_t)r);
     L.vpairs = align256(L.partials + (L.ks > 1 ? sizeof(float) * (size_t)L.tiles * L.ks *
                                                      kTileRows64 * (size_t)std::max(r, 16)
@@ -149,6 +169,7 @@ struct LayerProj {
 struct LayerArgs {
     LayerProj p[kMaxProjections];
     int num_projections;
+    WaitCtl wc;  // one status word for the whole call: the first projection's header
 };
 
 struct LayerProjIn {
@@ -179,6 +200,16 @@ inline size_t layer_workspace_total(const LayerProjIn *p, int num_projections, i
         total += align256(fused_layout(M, p[q].d_in, p[q].d_out, r, dtype).total);
     return total;
 }
+
+// Per-rank entry points, one translation unit each (R = 8, 16, 32, 64).
+template <int R>
+hipError_t launch_shrink_rank(const ShrinkArgs &a, hipStream_t stream);
+template <int R>
+hipError_t launch_expand_rank(const ExpandArgs &a, hipStream_t stream);
+template <int R>
+hipError_t launch_fused_rank(const FusedArgs &a, hipStream_t stream);
+template <int R>
+hipError_t launch_fused_layer_rank(const LayerCall &a, hipStream_t stream);
 
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs &a, hipStream_t stream);

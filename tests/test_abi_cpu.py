@@ -32,6 +32,21 @@ def test_symbol_exported(name):
     assert hasattr(sg.lib, name)
 
 
+def test_workspace_status_and_wait_limit_on_the_host():
+    # argument errors return before any HIP call
+    word = ctypes.c_uint32(0)
+    assert sg.lib.sgmv_workspace_status(None, ctypes.byref(word), None) == -1
+    assert sg.lib.sgmv_workspace_status(P1, None, None) == -1
+    # the limit is a process-wide setting: set, read back, restore
+    old = sg.sgmv_set_wait_limit(7)
+    try:
+        assert sg.sgmv_set_wait_limit(0) == 7
+        assert sg.sgmv_set_wait_limit(1 << 20) == 0
+    finally:
+        assert sg.sgmv_set_wait_limit(old) == 1 << 20
+    assert old == 1 << 15
+
+
 def test_status_strings():
     for st in range(-8, 1):
         assert sg.lib.sgmv_status_string(st)

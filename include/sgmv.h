@@ -87,7 +87,8 @@ enum sgmv_status {
     SGMV_ERR_ALIGN = -5,     /* X, Y or V not 16-byte aligned */
     SGMV_ERR_WORKSPACE = -6, /* workspace missing or smaller than sgmv_workspace_bytes */
     SGMV_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
-    SGMV_ERR_ADAPTER = -8    /* host metadata: an adapter id that is negative (or outside the pool) */
+    SGMV_ERR_ADAPTER = -8,   /* host metadata: an adapter id that is negative (or outside the pool) */
+    SGMV_ERR_SCRATCH = -9    /* sgmv_fused_noalloc: the batch needs more than SGMV_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -136,6 +137,31 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
                int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
                float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
                void *stream);
+
+/*
+ * sgmv_fused without a workspace argument and without any allocation: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments (minus the workspace), result and errors as sgmv_fused. The
+ * workspace is a static array of SGMV_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU (each GPU the call runs on holds its copy until the
+ * process ends); a batch whose fused workspace (sgmv_workspace_bytes) is
+ * larger is rejected with SGMV_ERR_SCRATCH and nothing is enqueued. The
+ * stream must belong to the current device. Each call first enqueues a
+ * one-workgroup kernel that zero-fills the array if an earlier call left a
+ * failure status in it (otherwise earlier calls left it zero), then the
+ * fused kernel. All calls on one GPU share the array: calls that overlap in
+ * time on that GPU (different streams, or different threads) race and must
+ * not be made; calls on one stream are ordered and safe. No hipMalloc,
+ * hipFree or allocating library routine is called.
+ */
+#define SGMV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int sgmv_fused_noalloc(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+                       int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                       int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r,
+                       float alpha, int32_t dtype, void *stream);
 
 /*
  * Gathered forms: the batch stays in token order (Punica guide, figure "CUDA

@@ -36,6 +36,8 @@ EXPORTS = {
     "sgmv_expand": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "sgmv_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _vp, _sz, _vp]),
+    "sgmv_fused_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _f32, _i32, _vp]),
     "sgmv_shrink_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _vp, _sz, _vp]),
     "sgmv_expand_scatter": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
@@ -231,6 +233,30 @@ def sgmv_fused(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: t
                         M, d_in, d_out, r, float(alpha), _dtype_code(X), ws, ws_bytes,
                         _stream(X, stream))
     _check("sgmv_fused", st)
+    return Y
+
+
+SGMV_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sgmv_fused_noalloc(Y: torch.Tensor, X: torch.Tensor, A_ptrs: torch.Tensor, B_ptrs: torch.Tensor,
+                       seg_start: torch.Tensor, seg_adapter: torch.Tensor, r: int, alpha: float,
+                       stream=None) -> torch.Tensor:
+    """sgmv_fused on the library's static per-device scratch array instead of
+    a workspace: nothing is allocated. Calls that overlap in time on one GPU
+    must not be made (they share the array)."""
+    M, d_in = X.shape
+    M2, d_out = Y.shape
+    if M2 != M:
+        raise ValueError("X and Y must have the same number of rows")
+    if A_ptrs.numel() != B_ptrs.numel():
+        raise ValueError("A_ptrs and B_ptrs must have one entry per adapter")
+    st = lib.sgmv_fused_noalloc(_dev(Y, "Y", dim=2), _dev(X, "X", dim=2),
+                                _dev(A_ptrs, "A_ptrs", torch.int64, 1), _dev(B_ptrs, "B_ptrs", torch.int64, 1),
+                                A_ptrs.numel(), _dev(seg_start, "seg_start", torch.int32, 1),
+                                _dev(seg_adapter, "seg_adapter", torch.int32, 1), seg_adapter.numel(),
+                                M, d_in, d_out, r, float(alpha), _dtype_code(X), _stream(X, stream))
+    _check("sgmv_fused_noalloc", st)
     return Y
 
 
@@ -468,4 +494,4 @@ __all__ = ["sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_shrink_gather", "sg
            "sgmv_workspace_bytes", "sgmv_build_segments",
            "sgmv_pool_pointers", "sgmv_version", "workspace", "SGMVError", "lib", "EXPORTS",
            "LIBRARY", "SGMV_F32", "SGMV_BF16", "sgmv_workspace_status", "sgmv_set_wait_limit",
-           "SGMV_WS_WAIT_TIMEOUT", "SGMV_WS_BAD_OFFSETS"]
+           "SGMV_WS_WAIT_TIMEOUT", "SGMV_WS_BAD_OFFSETS", "sgmv_fused_noalloc", "SGMV_NOALLOC_SCRATCH_BYTES"]

@@ -10,6 +10,7 @@
 
 #include "sgmv_launch.h"
 
+static_assert(SGMV_NOALLOC_SCRATCH_BYTES == sgmv::kScratchBytes, "scratch size of the header and the library agree");
 static_assert(SGMV_WS_WAIT_TIMEOUT == sgmv::kStatusTimeout && SGMV_WS_BAD_OFFSETS == sgmv::kStatusBadOffsets,
               "status bits of the header and the kernels agree");
 
@@ -51,6 +52,7 @@ const char *sgmv_status_string(int status) {
         case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
         case SGMV_ERR_HIP: return "HIP runtime error at launch";
         case SGMV_ERR_ADAPTER: return "adapter id negative or outside the pool";
+        case SGMV_ERR_SCRATCH: return "batch needs more workspace than the library's static scratch holds";
         default: return "unknown status";
     }
 }
@@ -134,6 +136,25 @@ int fused_call(void *Y, const void *X, const int32_t *rows, bool gathered, const
     return hip_status(sgmv::launch_fused(a, static_cast<hipStream_t>(stream)));
 }
 
+// sgmv_fused's checks, then the launch on the library's scratch array.
+int fused_noalloc_call(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+                       int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                       int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r, float alpha,
+                       int32_t dtype, void *stream) {
+    int st = check_common(num_adapters, num_segments, M, r, dtype);
+    if (st != SGMV_OK) return st;
+    if (!valid_dim(d_in) || !valid_dim(d_out) || (int64_t)M * d_in > kMaxElems ||
+        (int64_t)M * d_out > kMaxElems)
+        return SGMV_ERR_SHAPE;
+    if (M == 0 || num_segments == 0) return SGMV_OK;
+    if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
+    if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
+    if (sgmv::fused_layout(M, d_in, d_out, r, dtype).total > sgmv::kScratchBytes) return SGMV_ERR_SCRATCH;
+    sgmv::FusedArgs a{Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
+                      num_segments, M, d_in, d_out, r, dtype, alpha / (float)r, nullptr, nullptr};
+    return hip_status(sgmv::launch_fused_noalloc(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +181,14 @@ int sgmv_fused(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B
                void *stream) {
     return fused_call(Y, X, nullptr, false, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter,
                       num_segments, M, d_in, d_out, r, alpha, dtype, workspace, workspace_bytes, stream);
+}
+
+int sgmv_fused_noalloc(void *Y, const void *X, const uint64_t *A_ptrs, const uint64_t *B_ptrs,
+                       int32_t num_adapters, const int32_t *seg_start, const int32_t *seg_adapter,
+                       int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out, int32_t r, float alpha,
+                       int32_t dtype, void *stream) {
+    return fused_noalloc_call(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M, d_in,
+                              d_out, r, alpha, dtype, stream);
 }
 
 int sgmv_shrink_gather(float *V, const void *X, const int32_t *rows, const uint64_t *A_ptrs,

@@ -39,6 +39,7 @@
 //    tile's counters to zero. Every launch leaves the whole workspace zero.
 
 #include <atomic>
+#include <mutex>
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
@@ -1082,6 +1083,61 @@ hipError_t launch_expand(const ExpandArgs &a, hipStream_t st) { SGMV_RANK_SWITCH
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st) { SGMV_RANK_SWITCH(launch_fused_rank, a, st) }
 hipError_t launch_fused_layer(const LayerCall &a, hipStream_t st) {
     SGMV_RANK_SWITCH(launch_fused_layer_rank, a, st)
+}
+
+// ----------------------------------------------------------------------------
+// The fused call without a caller-supplied workspace: its workspace is a
+// file-scope device array, one per GPU the library runs on (each holds its
+// own copy at its own address until the process ends). Host code never uses
+// the array's name as an address: it looks the address up once per device
+// with hipGetSymbolAddress and passes that pointer on.
+// ----------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// One workgroup: if the scratch's status word says an earlier call failed,
+// zero all of it (leftovers of that call may lie anywhere in it); otherwise
+// every earlier call has left it zero and there is nothing to do. A kernel of
+// its own, not a memset, so that the call can be captured in a graph.
+__global__ __launch_bounds__(kBlock) void scratch_reset_kernel(uint4 *__restrict__ p, size_t vecs) {
+    __shared__ uint32_t s_status;
+    if (threadIdx.x == 0)
+        s_status = __hip_atomic_load(reinterpret_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_status == 0) return;
+    for (size_t i = threadIdx.x; i < vecs; i += kBlock) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on first use per device).
+static hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_fused_noalloc(FusedArgs a, hipStream_t st) {
+    void *ws = nullptr;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scratch_reset_kernel, dim3(1), dim3(kBlock), 0, st, static_cast<uint4 *>(ws),
+                       kScratchBytes / sizeof(uint4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.workspace = ws;
+    return launch_fused(a, st);
 }
 
 // How many polls a bounded wait makes before it gives up; read at each launch.

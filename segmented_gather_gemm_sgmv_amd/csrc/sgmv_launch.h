@@ -211,6 +211,12 @@ hipError_t launch_fused_rank(const FusedArgs &a, hipStream_t stream);
 template <int R>
 hipError_t launch_fused_layer_rank(const LayerCall &a, hipStream_t stream);
 
+// The fused call on the library's own per-device scratch array (a.workspace
+// is ignored): for callers that cannot allocate. The batch's fused workspace
+// must fit in kScratchBytes.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t launch_fused_noalloc(FusedArgs a, hipStream_t stream);
+
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs &a, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t stream);

@@ -48,7 +48,7 @@ def test_workspace_status_and_wait_limit_on_the_host():
 
 
 def test_status_strings():
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert sg.lib.sgmv_status_string(st)
     assert sg.lib.sgmv_status_string(-99) == b"unknown status"
 

@@ -84,8 +84,17 @@ __device__ __forceinline__ void store_v_flagged(float *V, size_t idx, float v) {
     __hip_atomic_store(reinterpret_cast<uint64_t *>(V) + idx, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The workspace's sticky status word (NULL when the call has no workspace).
+// The workspace's sticky status word (NULL when the call has no workspace),
+// as earlier calls left it: read at a workgroup's start with a plain load
+// (the kernel boundary makes earlier launches' writes visible; a plain load
+// may be served by the L2 its XCD shares, where a device-scope one would go
+// to memory from every workgroup).
 __device__ __forceinline__ uint32_t read_status(const WaitCtl &wc) {
+    return wc.status ? *wc.status : 0u;
+}
+
+// The status word as it is now, failures of this launch included.
+__device__ __forceinline__ uint32_t read_status_now(const WaitCtl &wc) {
     return wc.status ? __hip_atomic_load(wc.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 }
 
@@ -104,7 +113,7 @@ __device__ __forceinline__ bool give_up(const WaitCtl &wc, uint32_t spins, bool 
         if (lead) report(wc, kStatusTimeout);
         return true;
     }
-    if ((spins & 31) == 31) return __builtin_amdgcn_readfirstlane((int)read_status(wc)) != 0;
+    if ((spins & 31) == 31) return __builtin_amdgcn_readfirstlane((int)read_status_now(wc)) != 0;
     return false;
 }
 
@@ -246,9 +255,11 @@ __device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_ad
 // One vector-path shrink item: rank row j of segment s, one wave. Returns
 // false if the segment is empty, names no valid adapter or belongs to the
 // MFMA path (then nothing is written).
-// The workspace status is read with the metadata: a non-zero status (an
-// earlier failure) makes the item a no-op. Offsets that decrease at this
-// segment (so that other segments may overlap) are reported, once.
+// Offsets that decrease at this segment (so that other segments may overlap)
+// are reported, once. In a separate shrink launch a non-zero workspace
+// status (an earlier failure) makes the item a no-op; in the fused launch
+// (kFlagged) the consumers check it instead, where their check costs no
+// latency: a producer's V in a failed workspace is never read.
 template <typename T, int R, bool kFlagged, bool kSpec, typename RM>
 __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const uint64_t *A_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
@@ -258,7 +269,7 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     AdapterTable<kSpec> tab;
     tab.load(A_ptrs, num_adapters, lane);
     int lo, hi;
-    const uint32_t st = read_status(wc);
+    const uint32_t st = kFlagged ? 0u : read_status(wc);
     const int k = seg_adapter[s];
     const bool inverted = segment_rows(seg_start, s, M, lo, hi);
     if (inverted && j == 0 && lane == 0) report(wc, kStatusBadOffsets);
@@ -332,7 +343,96 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
     }
 }
 
-// One MFMA shrink item: part `kp` (of `ks`) of d_in for the 64-row tile `t`.
+// One MFMA shrink item: part `kp` (of `ks`) of d_in for column group `cg` of
+// piece `pi` of the 16-row tile `t` (the shrink unit u; see
+// mfma_shrink_item). With ks == 1 the result goes straight to V. Otherwise each part leaves its 16 x R partial
+// tile in the workspace, in the MFMA D layout (fragment f = 64 b + lane holds
+// four values, 16 bytes), counts itself in at *split_counter and waits for
+// the other parts. Then every part finishes its own share of the fragments:
+// it sums them over the parts in the order 0 .. ks-1, writes those V entries
+// and clears those fragments in every part, so the tile's combine is spread
+// over ks workgroups. The counter's return to zero is described below.
+//
+// The wait ends: the parts of a tile have consecutive workgroup ids,
+// workgroups are dispatched in id order, and at most one tile straddles the
+// dispatch front, with fewer parts than the device has slots, so every part
+// of a waiting tile is dispatched. If the bound runs out all the same (a
+// corrupt counter), the part skips its share and returns 0. Returns 1 (to
+// all threads) once this workgroup's V entries are stored.
+// kSelfReset: a second count lets the last part out return the split
+// counter to zero. Without it (the fused kernel) the counter is left at ks
+// for the tile's last expand workgroup to reset: the expand workgroups start
+// only once every part has published, i.e. has passed its wait, and the
+// part's own departure round trip stays off the path to its V handoff.
+template <int R, bool kCoherent, bool kSelfReset, typename AkOf, typename RM>
+__device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
+                                const Piece &pc, int d_in, int t, int cg, int u, int kp, int ks,
+                                uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
+                                int *s_flag, RM rm, const WaitCtl &wc) {
+    constexpr int NB = ShrinkSmem<R>::kNBW;
+    constexpr int kFrags = NB * kWave;  // 16-byte fragments per partial tile
+    constexpr uint32_t kTileBytes = kFrags * 16;
+    static_assert(kFrags <= kBlock, "one fragment per thread");
+    const int t0 = t * kShrinkRows;
+    const int nsteps = (d_in + ShrinkSmem<R>::kStepK - 1) / ShrinkSmem<R>::kStepK;
+    const int per = (nsteps + ks - 1) / ks;
+    const int s0 = min(nsteps, kp * per);
+    const int s1 = min(nsteps, s0 + per);
+    f32x4_t res = {0.f, 0.f, 0.f, 0.f};
+    shrink_tile_mfma<R>(X, ak_of(pc.k), d_in, t0, pc.lo, pc.hi, cg, s0, s1, sm, res, rm);
+    auto in_pieces = [&](int m) { return m >= pc.lo && m < pc.hi; };
+    // fragment f = 64 b + lane, lane = (i, g): rows t0 + 4 g + v (v < 4),
+    // column 16 (NB cg + b) + i
+    auto store_frag = [&](int f, const f32x4_t &val) {
+        const int lane = f % kWave, b = f / kWave;
+        const int j = 16 * (NB * cg + b) + (lane & 15);
+        if (j >= R) return;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = t0 + 4 * (lane >> 4) + v;
+            if (in_pieces(m)) store_v<kCoherent>(V + (size_t)m * R + j, val[v]);
+        }
+    };
+    const int tid = threadIdx.x;
+    if (ks == 1) {
+        if (tid < kFrags) store_frag(tid, res);
+        return 1;
+    }
+    float *tile_parts = partials + (size_t)u * ks * (kTileBytes / 4);
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(tile_parts, (uint32_t)ks * kTileBytes);
+    if (tid < kFrags) store4_coherent(rs, (uint32_t)kp * kTileBytes + (uint32_t)tid * 16, res);
+    publish(split_counter);
+    if (!wait_for(split_counter, (uint32_t)ks, s_flag, wc)) return 0;
+    // This part's share: fragments [f0, f1). Every part of a fragment is
+    // requested before it is summed or cleared: a load placed after a store
+    // to the same buffer would wait for that store.
+    constexpr int kMaxParts = 8;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const int f0 = kp * kFrags / ks, f1 = (kp + 1) * kFrags / ks;
+    for (int f = f0 + tid; f < f1; f += kBlock) {
+        f32x4_t pv[kMaxParts];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) pv[k] = load4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16);
+        f32x4_t sum = zero;
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) sum += pv[k];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k)
+            if (k < ks) store4_coherent(rs, (uint32_t)k * kTileBytes + (uint32_t)f * 16, zero);
+        store_frag(f, sum);
+    }
+    // every part has seen the full count once all of them have counted out
+    if constexpr (kSelfReset) {
+        if (depart_last(split_counter, 2u * (uint32_t)ks, s_flag) && threadIdx.x == 0)
+            __hip_atomic_store(split_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return 1;
+}
+
+// One MFMA shrink item of a 64-row tile: part `kp` (of `ks`) of d_in for the
+// 64-row tile `t`.
 // With ks == 1 the result goes straight to V. Otherwise each part leaves its
 // 64 x R partial tile in the workspace, in the MFMA D layout (fragment f =
 // (wave * NB + b) * 64 + lane holds four values, 16 bytes), counts itself in
@@ -355,11 +455,11 @@ __device__ __forceinline__ void reset_pair(uint32_t *a, uint32_t *b) {
 // only once every part has published, i.e. has passed its wait, and the
 // part's own departure round trip stays off the path to its V handoff.
 template <int R, bool kCoherent, bool kSelfReset, typename AkOf, typename RM>
-__device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
+__device__ int shrink_mfma_item64(float *V, const bf16_t *X, AkOf ak_of,
                                 const PieceList &pl, int d_in, int t, int kp, int ks,
-                                uint32_t *split_counter, float *partials, ShrinkSmem<R> &sm,
+                                uint32_t *split_counter, float *partials, Shrink64Smem<R> &sm,
                                 int *s_flag, RM rm, const WaitCtl &wc) {
-    constexpr int NB = ShrinkSmem<R>::kNB;
+    constexpr int NB = Shrink64Smem<R>::kNB;
     constexpr int kFrags = kWavesPerBlock * NB * kWave;  // 16-byte fragments per partial tile
     constexpr uint32_t kTileBytes = kFrags * 16;
     const int t0 = t * kShrinkTileRows;
@@ -377,11 +477,11 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
             const Piece p1 = pl.p[q + 1];
             const bf16_t *const ak[2] = {ak_of(p0.k), ak_of(p1.k)};
             const int lo[2] = {p0.lo, p1.lo}, hi[2] = {p0.hi, p1.hi};
-            shrink_tile_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
+            shrink_tile64_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
         } else {
             const bf16_t *const ak[1] = {ak_of(p0.k)};
             const int lo[1] = {p0.lo}, hi[1] = {p0.hi};
-            shrink_tile_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
+            shrink_tile64_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
         }
     }
     auto in_pieces = [&](int m) {
@@ -444,6 +544,26 @@ __device__ int shrink_mfma_item(float *V, const bf16_t *X, AkOf ak_of,
     return 1;
 }
 
+// The MFMA shrink items of a launch: num_units shrink units (a 16-row tile,
+// one of the long segments it meets and a group of V columns; unit u =
+// (2 t + piece) kGroups + group), ks parts each. With one part,
+// units are numbered so that each XCD takes a contiguous run of them
+// (consecutive tiles belong to the same segments and read the same adapter,
+// which then stays in one L2); the run is launched rounded up to a multiple
+// of 8. With several parts, the parts of a unit have consecutive ids (they
+// wait for one another) and part kp of every unit runs on XCD kp. Returns
+// false for padding ids.
+__device__ __forceinline__ bool mfma_shrink_item(int item, int first, int num_units, int ks, int &u, int &kp) {
+    if (ks == 1) {
+        u = xcd_local_item(item, first, num_units);
+        kp = 0;
+        return u >= 0;
+    }
+    u = (item - first) / ks;
+    kp = (item - first) % ks;
+    return u < num_units;
+}
+
 // Vector shrink items: segment s, rank group g (of `groups`), numbered so
 // that all groups of one segment get ids of the same residue mod 8, i.e.
 // run on one XCD (workgroups are dealt to the XCDs round-robin by id) and
@@ -467,21 +587,23 @@ struct MfmaAdapters {
     __device__ __forceinline__ MfmaAdapters(const uint64_t *p, int n) : ptrs(p), num_adapters(n) {
         tab.load(p, n, threadIdx.x & (kWave - 1));
     }
-    // k: a valid adapter id, uniform across the workgroup
+    // k: a valid adapter id, uniform across the workgroup (read from LDS, so
+    // made explicitly uniform: the table lookup selects a lane by it)
     __device__ __forceinline__ const bf16_t *operator()(int k) const {
+        k = __builtin_amdgcn_readfirstlane(k);
         return reinterpret_cast<const bf16_t *>(num_adapters <= kSpecTable ? tab.address(ptrs, k) : ptrs[k]);
     }
 };
 
 // Items [0, round_up_xcds(N) * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
-// one per (64-row tile, part of d_in) (bf16 only).
+// one per (16-row tile, part of d_in) (bf16 only).
 template <typename T, int R, bool kGather>
 __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
-    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int ks,
-    uint32_t *counters, float *partials, RowMap<kGather> rm, WaitCtl wc) {
+    const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int num_units, int ks,
+    int small, uint32_t *counters, float *partials, RowMap<kGather> rm, WaitCtl wc) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = round_up_xcds(num_segments) * groups;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -499,24 +621,35 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         return;
     }
     if constexpr (Elem<T>::kMfma) {
-        __shared__ ShrinkSmem<R> sm;
+        __shared__ union {
+            ShrinkSmem<R> s16;
+            Shrink64Smem<R> s64;
+        } sm;
         __shared__ PieceList pl;
         __shared__ int s_flag;
-        const int tiles = (M + kShrinkTileRows - 1) / kShrinkTileRows;
-        // parts of a tile have consecutive ids; with ks = 8, part kp of every
-        // tile runs on XCD kp (ids are dealt to the XCDs round-robin), where
-        // the tiles of a segment share slice kp of its A_k in one L2
-        const int t = ((int)blockIdx.x - gemv_items) / ks, kp = ((int)blockIdx.x - gemv_items) % ks;
-        if (t >= tiles) return;
-        const int t0 = t * kShrinkTileRows;
+        int u, kp;
+        if (!mfma_shrink_item((int)blockIdx.x, gemv_items, num_units, ks, u, kp)) return;
         const uint32_t st = read_status(wc);
         const MfmaAdapters ak_of(A_ptrs, num_adapters);
-        gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
-                             min(t0 + kShrinkTileRows, M));
-        if (pl.n == 0 || st != 0) return;
-        shrink_mfma_item<R, false, true>(V, reinterpret_cast<const bf16_t *>(X), ak_of, pl, d_in, t,
-                                   kp, ks, ks > 1 ? counters + (size_t)t * kCounterStride : nullptr,
-                                   partials, sm, &s_flag, rm, wc);
+        const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
+        uint32_t *const split = ks > 1 ? counters + (size_t)u * kCounterStride : nullptr;
+        if (small) {
+            constexpr int CG = ShrinkSmem<R>::kGroups;
+            const int cg = u % CG, pi = (u / CG) % kShrinkPieces, t = u / (CG * kShrinkPieces);
+            const int t0 = t * kShrinkRows;
+            gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
+                                 min(t0 + kShrinkRows, M));
+            if (pi >= pl.n || st != 0) return;
+            shrink_mfma_item<R, false, true>(V, Xb, ak_of, pl.p[pi], d_in, t, cg, u, kp, ks, split, partials,
+                                             sm.s16, &s_flag, rm, wc);
+        } else {
+            const int t0 = u * kShrinkTileRows;
+            gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
+                                 min(t0 + kShrinkTileRows, M));
+            if (pl.n == 0 || st != 0) return;
+            shrink_mfma_item64<R, false, true>(V, Xb, ak_of, pl, d_in, u, kp, ks, split, partials, sm.s64, &s_flag,
+                                               rm, wc);
+        }
     }
 }
 
@@ -624,8 +757,10 @@ __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn,
 
 // One vector-path expand item: columns n0 .. n0 + VEC - 1 (per thread) of
 // segment s; `ready` as for expand_segment. Returns false if the segment is
-// empty, names no valid adapter, belongs to the MFMA path or the workspace
-// status is not zero. lo, hi receive the segment's rows.
+// empty, names no valid adapter or belongs to the MFMA path. In the fused
+// launch (kFlagged) a non-zero workspace status, checked once B and Y are
+// requested and before V is read, leaves its rows untouched (and returns
+// false). lo, hi receive the segment's rows.
 template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn, typename RM>
 __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
@@ -634,13 +769,21 @@ __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const u
                                                    ReadyFn ready, RM rm, const WaitCtl &wc) {
     AdapterTable<kSpec> tab;
     tab.load(B_ptrs, num_adapters, threadIdx.x & (kWave - 1));
-    const uint32_t st = read_status(wc);
     const int k = seg_adapter[s];
     segment_rows(seg_start, s, M, lo, hi);
-    if (!vector_segment<T>(lo, hi, k, num_adapters) | (st != 0)) return false;
+    if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
-    expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm, wc);
-    return true;
+    if constexpr (kFlagged) {
+        // requested after the metadata: loads complete in order, so waiting
+        // for the metadata does not wait for it too
+        const uint32_t st = read_status(wc);
+        auto ready_ok = [st, &ready]() { return st == 0 && ready(); };
+        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready_ok, rm, wc);
+        return st == 0;
+    } else {
+        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm, wc);
+        return true;
+    }
 }
 
 // Items [0, N * ntiles_g): vector path, one per (segment, tile of
@@ -719,24 +862,26 @@ __device__ __forceinline__ void fused_item(
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials, RowMap<kGather> rm, const WaitCtl &wc, const int item) {
+    int num_units, int ks, int small, float scale, int long_batch, uint32_t *tile_counters,
+    uint32_t *split_counters, float *Vws, float *Vpairs, float *partials, RowMap<kGather> rm, const WaitCtl &wc,
+    const int item) {
     // The vector path hands V over as flagged pairs (Vpairs), one copy per
     // expand column tile, so each expand workgroup clears its own copy with
-    // no counter. Each 64-row tile owns one cache line of counters: word 0
-    // counts the shrink parts whose V entries are stored (polled by the
-    // expand workgroups until it reaches ks), word 1 counts expand
-    // departures, word 2 synchronises the parts of a split shrink (and is
-    // reset, with the others, by the tile's last expand workgroup).
+    // no counter. Each 64-row expand tile owns one cache line of counters:
+    // word 0 counts the shrink parts whose V entries for its rows are stored
+    // (of the shrink units of its four 16-row tiles, or of the 64-row tile),
+    // polled by the expand workgroups until every part of every unit has
+    // counted in; word 1 counts expand departures. A split unit's parts
+    // synchronise on a line of their own (split_counters); the last expand
+    // workgroup of a 64-row tile resets all of these.
     uint32_t *const tile_arrive = tile_counters;
     uint32_t *const tile_depart = tile_counters + 1;
-    uint32_t *const tile_split = tile_counters + 2;
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
     const int a0 = round_up_xcds(num_segments) * groups;  // vector shrink items
-    const int a1 = a0 + num_tiles * ks;                   // MFMA shrink items (64 rows x part)
+    const int a1 = a0 + mfma_shrink_items(num_units, ks);  // MFMA shrink items (unit x part)
     const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
 
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -779,24 +924,42 @@ __device__ __forceinline__ void fused_item(
     }
     if constexpr (Elem<T>::kMfma) {
         __shared__ union {
-            ShrinkSmem<R> shrink;
+            ShrinkSmem<R> s16;
+            Shrink64Smem<R> s64;
             ExpandSmem<R> expand;
         } sm;
         __shared__ PieceList pl;
         const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
         if (item >= a0 && item < a1) {
-            // (64-row tile, part of d_in); each part reports its share of
-            // the tile's V on the tile's arrival word
-            const int t = (item - a0) / ks, kp = (item - a0) % ks;
-            const int t0 = t * kShrinkTileRows;
+            // (shrink unit, part of d_in); each part reports its share of V
+            // on the arrival word of the 64-row tile holding these rows
+            int u, kp;
+            if (!mfma_shrink_item(item, a0, num_units, ks, u, kp)) return;
             const uint32_t st = read_status(wc);
             const MfmaAdapters ak_of(A_ptrs, num_adapters);
-            gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
-                                 t0, min(t0 + kShrinkTileRows, M));
-            if (pl.n == 0 || st != 0) return;
-            if (shrink_mfma_item<R, true, false>(Vws, Xb, ak_of, pl, d_in, t, kp, ks,
-                                          &tile_split[t * kCounterStride], partials, sm.shrink, &s_flag, rm, wc))
-                publish(&tile_arrive[t * kCounterStride]);
+            uint32_t *const split = ks > 1 ? split_counters + (size_t)u * kCounterStride : nullptr;
+            int done;
+            int t64;
+            if (small) {
+                constexpr int CG = ShrinkSmem<R>::kGroups;
+                const int cg = u % CG, pi = (u / CG) % kShrinkPieces, t = u / (CG * kShrinkPieces);
+                const int t0 = t * kShrinkRows;
+                gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
+                                     t0, min(t0 + kShrinkRows, M));
+                if (pi >= pl.n || st != 0) return;
+                done = shrink_mfma_item<R, true, false>(Vws, Xb, ak_of, pl.p[pi], d_in, t, cg, u, kp, ks, split,
+                                                        partials, sm.s16, &s_flag, rm, wc);
+                t64 = t0 / kTileRows;
+            } else {
+                const int t0 = u * kShrinkTileRows;
+                gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
+                                     t0, min(t0 + kShrinkTileRows, M));
+                if (pl.n == 0 || st != 0) return;
+                done = shrink_mfma_item64<R, true, false>(Vws, Xb, ak_of, pl, d_in, u, kp, ks, split, partials,
+                                                          sm.s64, &s_flag, rm, wc);
+                t64 = u;
+            }
+            if (done) publish(&tile_arrive[t64 * kCounterStride]);
             return;
         }
         const int e = xcd_local_item(item, a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
@@ -807,12 +970,25 @@ __device__ __forceinline__ void fused_item(
         const int n0 = (e % ntiles_m) * kExpandTileCols;
         const uint32_t st = read_status(wc);
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
-        // the shrink tile with the same rows is done once all its parts report;
+        // V of these rows is complete once every part of every shrink unit
+        // inside them has reported: kGroups units per 16-row tile and long
+        // segment meeting it (the shrink tiles find the same long segments);
         // a non-zero status on entry makes the tile a no-op
         int state = -1;  // uniform: -1 not yet waited, else the result of the wait
         auto ready = [&]() {
-            if (state < 0)
-                state = st == 0 && wait_for(&tile_arrive[t * kCounterStride], (uint32_t)ks, &s_flag, wc);
+            if (state < 0) {
+                int units = 1;  // 64-row tiles: the tile itself
+                if (small) {
+                    units = 0;
+                    for (int a = t0; a < t1; a += kShrinkRows) {
+                        const int b = min(a + kShrinkRows, t1);
+                        for (int q = 0; q < pl.n; ++q) units += pl.p[q].lo < b && pl.p[q].hi > a;
+                    }
+                    units *= ShrinkSmem<R>::kGroups;
+                }
+                state = st == 0 &&
+                        wait_for(&tile_arrive[t * kCounterStride], (uint32_t)(ks * units), &s_flag, wc);
+            }
             return state != 0;
         };
         // V of this tile's rows, read at device scope (written in this launch)
@@ -841,10 +1017,15 @@ __device__ __forceinline__ void fused_item(
         if (depart_last(&tile_depart[t * kCounterStride], (uint32_t)ntiles_m, &s_flag)) {
             for (int q = 0; q < pl.n; ++q) zero_rows(Vws, pl.p[q].lo, pl.p[q].hi, R);
             reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
-            // the split counter too: its parts all passed their wait before publishing
-            if (ks > 1 && tid == 0)
-                __hip_atomic_store(&tile_split[t * kCounterStride], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            // the split counters of its shrink tiles too: their parts all
+            // passed their wait before publishing
+            const int units_per_tile = small ? ShrinkSmem<R>::kGroups * kShrinkPieces * kTileRows / kShrinkRows : 1;
+            if (ks > 1 && tid < units_per_tile) {
+                const int u = units_per_tile * t + tid;
+                if (u < num_units)
+                    __hip_atomic_store(split_counters + (size_t)u * kCounterStride, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -855,11 +1036,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int ks, float scale, int long_batch, uint32_t *tile_counters, float *Vws,
-    float *Vpairs, float *partials, RowMap<kGather> rm, WaitCtl wc) {
+    int num_units, int ks, int small, float scale, int long_batch, uint32_t *tile_counters,
+    uint32_t *split_counters, float *Vws, float *Vpairs, float *partials, RowMap<kGather> rm, WaitCtl wc) {
     fused_item<T, R, kGather>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
-                              d_in, d_out, ntiles_g, ntiles_m, num_tiles, ks, scale, long_batch,
-                              tile_counters, Vws, Vpairs, partials, rm, wc, (int)blockIdx.x);
+                              d_in, d_out, ntiles_g, ntiles_m, num_tiles, num_units, ks, small, scale, long_batch,
+                              tile_counters, split_counters, Vws, Vpairs, partials, rm, wc, (int)blockIdx.x);
 }
 
 // Layer-batched fused launch (the launch accounting of the Punica guide's
@@ -874,22 +1055,64 @@ template <typename T, int R, bool kGather>
 __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
     LayerArgs L, const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, float scale, int long_batch, RowMap<kGather> rm) {
+    // The descriptors are read in place, in the kernel argument segment (L
+    // is the first argument, at offset 0): indexing the by-value copy with a
+    // computed index can make the compiler copy the whole argument to the
+    // stack.
+    using ConstProj = const __attribute__((address_space(4))) LayerProj;
+    ConstProj *kargs = (ConstProj *)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
     int p = 0;
-    for (int q = 1; q < L.num_projections; ++q) p = b >= L.p[q].base ? q : p;
-    const LayerProj &d = L.p[p];
+    for (int q = 1; q < L.num_projections; ++q) p = b >= kargs[q].base ? q : p;
+    p = __builtin_amdgcn_readfirstlane(p);
+    // The selected descriptor, field by field, as explicitly uniform values:
+    // read through the computed index, some fields would otherwise be kept
+    // in vector registers, where the pointers that feed buffer resources
+    // (which must be scalar) cannot be.
+    LayerProj d;
+    {
+        ConstProj &src = kargs[p];
+        auto up = [](auto *ptr) {
+            const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+            const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+            const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+            return reinterpret_cast<decltype(ptr)>((hi << 32) | lo);
+        };
+        auto ui = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+        d.Y = up(src.Y);
+        d.X = up(src.X);
+        d.A_ptrs = up(src.A_ptrs);
+        d.B_ptrs = up(src.B_ptrs);
+        d.tile_counters = up(src.tile_counters);
+        d.split_counters = up(src.split_counters);
+        d.Vws = up(src.Vws);
+        d.Vpairs = up(src.Vpairs);
+        d.partials = up(src.partials);
+        d.num_adapters = ui(src.num_adapters);
+        d.d_in = ui(src.d_in);
+        d.d_out = ui(src.d_out);
+        d.ntiles_g = ui(src.ntiles_g);
+        d.ntiles_m = ui(src.ntiles_m);
+        d.num_tiles = ui(src.num_tiles);
+        d.num_units = ui(src.num_units);
+        d.ks = ui(src.ks);
+        d.small = ui(src.small);
+        d.base = ui(src.base);
+        d.items = ui(src.items);
+    }
     const int item = b - d.base;
     if (item >= d.items) return;  // padding up to the next region
     fused_item<T, R, kGather>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
                               d.B_ptrs, d.num_adapters, seg_start, seg_adapter, num_segments, M, d.d_in,
-                              d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.ks, scale, long_batch,
-                              d.tile_counters, d.Vws, d.Vpairs, d.partials, rm, L.wc, item);
+                              d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.num_units, d.ks, d.small, scale,
+                              long_batch,
+                              d.tile_counters, d.split_counters, d.Vws, d.Vpairs, d.partials, rm, L.wc, item);
 }
 
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
-static_assert(kTileRows64 == kTileRows && kTileRows64 == kShrinkTileRows && kMacroSteps == kMacroK,
+static_assert(kTileRows64 == kTileRows && kShrinkRows16 == kShrinkRows,
               "workspace layouts must match the MFMA tiles");
 
 static int mfma_tiles(int dtype, int M) { return dtype == kBF16 ? (M + kTileRows - 1) / kTileRows : 0; }
@@ -904,15 +1127,16 @@ static int gemv_col_tiles(int d_out) {
 template <typename T, int R, bool kGather>
 static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
-    const int tiles = Elem<T>::kMfma ? L.tiles : 0;
-    const unsigned grid =
-        (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + (unsigned)tiles * L.ks;
+    const int units = Elem<T>::kMfma ? L.plan.units : 0;
+    const int ks = L.plan.ks;
+    const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
+                          (unsigned)(units ? mfma_shrink_items(units, ks) : 0);
     char *ws = static_cast<char *>(a.workspace);
     hipLaunchKernelGGL((shrink_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.num_segments, a.M, a.d_in, L.ks,
-                       L.ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
-                       L.ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr,
+                       a.seg_adapter, a.num_segments, a.M, a.d_in, units, ks, L.plan.small,
+                       ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
+                       ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr,
                        RowMap<kGather>{a.rows, a.M},
                        WaitCtl{L.total > 0 ? reinterpret_cast<uint32_t *>(ws) : nullptr, wait_limit()});
     return hipGetLastError();
@@ -954,19 +1178,21 @@ template <typename T, int R, bool kGather>
 static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
     const FusedLayout L = fused_layout(a.M, a.d_in, a.d_out, a.r, a.dtype);
     const int tiles = Elem<T>::kMfma ? L.tiles : 0;
+    const int units = Elem<T>::kMfma ? L.plan.units : 0;
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
     if (ntiles_g != L.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
-                          (unsigned)tiles * L.ks +
+                          (unsigned)(units ? mfma_shrink_items(units, L.plan.ks) : 0) +
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
     hipLaunchKernelGGL((fused_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, L.ks, a.scale,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, units, L.plan.ks, L.plan.small, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), tile_c,
+                       reinterpret_cast<uint32_t *>(ws + L.split_counters),
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
                        reinterpret_cast<float *>(ws + L.partials), RowMap<kGather>{a.rows, a.M},
                        WaitCtl{reinterpret_cast<uint32_t *>(ws), wait_limit()});
@@ -998,18 +1224,23 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         d.d_in = in.d_in;
         d.d_out = in.d_out;
         const int tiles = Elem<T>::kMfma ? FL.tiles : 0;
+        const int units = Elem<T>::kMfma ? FL.plan.units : 0;
         d.ntiles_g = gemv_col_tiles<T>(in.d_out);
         if (d.ntiles_g != FL.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
         d.ntiles_m = tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
         d.num_tiles = tiles;
-        d.ks = FL.ks;
+        d.num_units = units;
+        d.ks = FL.plan.ks;
+        d.small = FL.plan.small;
         char *w = ws + ws_off;
         d.tile_counters = reinterpret_cast<uint32_t *>(w + FL.tile_counters);
+        d.split_counters = reinterpret_cast<uint32_t *>(w + FL.split_counters);
         d.Vws = reinterpret_cast<float *>(w + FL.v);
         d.Vpairs = reinterpret_cast<float *>(w + FL.vpairs);
         d.partials = reinterpret_cast<float *>(w + FL.partials);
-        d.items = round_up_xcds(a.num_segments) * (R / kWavesPerBlock) + tiles * FL.ks +
-                  a.num_segments * d.ntiles_g + round_up_xcds(tiles * d.ntiles_m);
+        d.items = round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
+                  (units ? mfma_shrink_items(units, FL.plan.ks) : 0) + a.num_segments * d.ntiles_g +
+                  round_up_xcds(tiles * d.ntiles_m);
         d.base = base;
         base += round_up_xcds(d.items);
         ws_off += align256(FL.total);

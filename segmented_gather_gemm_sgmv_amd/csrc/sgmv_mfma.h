@@ -213,7 +213,201 @@ __device__ void gather_pieces(PieceList &pl, const SegPrefetch &pre, const int32
 }
 
 // ----------------------------------------------------------------------------
-// Shrink tile: V[m, 0:R] = X[m, :] . A_k for the rows m of up to two pieces
+// Two shrink tiles. A batch of many tiles (a prefill batch) takes 64-row
+// tiles: the A_k chunk of a step is shared by the four waves (each owns 16
+// rows) through LDS, so A_k crosses the L1 once per 64 rows, and d_in is
+// split between workgroups to fill the chip. A batch of few tiles (a few
+// mid-length segments) takes 16-row tiles with the four waves splitting
+// d_in: A_k crosses the L1 once per 16 rows, which matters little at r <= 32
+// and few tiles, and there is no cross-workgroup combine on the way to V.
+// ----------------------------------------------------------------------------
+// ----------------------------------------------------------------------------
+// 16-row shrink tile (batches of few tiles): V[m, 0:R] = X[m, :] . A_k for
+// the rows m of one piece (a long
+// segment's rows inside the tile) of the 16-row tile starting at t0, over
+// the steps [s_begin, s_end) of d_in (ShrinkSmem<R>::kStepK elements each). The tile size follows the
+// segments: a 16-row tile wastes at most 15 rows at a segment's end, where a
+// 64-row tile (prefill-sized) would waste up to 63 and leave too few tiles to
+// spread a few mid-length segments over the chip.
+//
+// The four waves split the steps between them (wave w takes the w-th
+// contiguous quarter) and each keeps its own 16 x R partial tile; the
+// partials meet in LDS once, at the end, and are summed in the fixed order of
+// the waves. No wave waits for another inside the loop.
+//
+// Loads are row-contiguous: in a step, 16 lanes cover the 256 bytes of one
+// row (X row or A_k rank row), so each load instruction reads four whole
+// row chunks. (Loading straight into the MFMA operand layout would make
+// every instruction touch 16 rows, 64 bytes each, 8 KB apart, which streams
+// several times slower.) Each wave stages its step in its own LDS buffer,
+// chunk c of row rho in slot c ^ (rho % 16), and reads the operands back in
+// the MFMA layout: in slice q (elements 32 q .. 32 q + 31 of the step) lane
+// (i, g) takes chunk 4 q + g of X row i and of A_k rank row 16 b + i. The
+// XOR makes both the writes (16 lanes per row, a permutation of its slots)
+// and the reads (16 rows, distinct slots) free of bank conflicts. LDS
+// operations of one wave complete in order, so the wave needs no barrier
+// between writing its buffer and reading it, nor before rewriting it.
+//
+// kStages steps are in flight per lane in a ring of registers. Every load is
+// unconditional: a chunk past d_in or a step past the wave's range loads a
+// clamped address and is staged as zeros (for X and A_k alike, so that a
+// non-finite value cannot leak into the sum); rows outside the piece load a
+// row of the piece and are never stored.
+// ----------------------------------------------------------------------------
+constexpr int kShrinkRows = 16;   // rows of an MFMA shrink tile (one MFMA's M)
+
+template <int R>
+struct ShrinkSmem {
+    static constexpr int kNB = R < 16 ? 1 : R / 16;                 // 16-column MFMA blocks of V
+    // Blocks one workgroup computes: at most two (32 columns), so that r = 64
+    // takes two workgroups per tile, each reading X and half of A_k: enough
+    // work items to fill the chip, and an 80-row step would need more
+    // registers and LDS than leave two workgroups per CU.
+    static constexpr int kNBW = kNB < 2 ? kNB : 2;
+    static constexpr int kGroups = kNB / kNBW;                      // column groups per tile
+    static constexpr int kRows = kShrinkRows + 16 * kNBW;           // staged rows: X, then A_k
+    static constexpr int kStepK = 128;                              // d_in elements per step
+    static constexpr int kCpr = kStepK / 8;                         // 16-byte chunks per row and step
+    static constexpr int kRpi = kWave / kCpr;                       // rows per load instruction
+    static constexpr int kLoads = kRows / kRpi;                     // row-contiguous loads per lane and step
+    static constexpr int kStages = kLoads <= 8 ? 4 : 3;             // steps in flight
+    static constexpr int kWaves = kBlockThreads / kWave;
+    union {
+        uint4 stage[kWaves][kRows * kCpr];      // each wave's staged step
+        f32x4_t part[kWaves][kNBW][kWave];      // each wave's partial tile, after the loop
+    };
+};
+
+template <int NL>
+struct ShrinkStage {
+    uint4 v[NL];     // rows kRpi l + lane / kCpr (l < NL), chunk lane % kCpr
+    uint32_t keep;   // all ones if the chunk lies inside d_in and the step inside the wave's range, else 0
+};
+
+// One wave's partial tile over its steps, for the 16 kNBW columns of column
+// group cg; acc is in the MFMA D layout (lane (i, g) holds rows 4 g + v,
+// v < 4, of column 16 (kNBW cg + b) + i).
+template <int R, typename RM>
+__device__ __forceinline__ void shrink_wave_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int lo,
+                                                 int hi, int cg, int s_begin, int s_end, ShrinkSmem<R> &sm,
+                                                 f32x4_t (&acc)[ShrinkSmem<R>::kNBW], RM rm) {
+    using SM = ShrinkSmem<R>;
+    constexpr int NB = SM::kNBW;
+    constexpr int NL = SM::kLoads;
+    constexpr int S = SM::kStages;
+    constexpr int W = SM::kWaves;
+    constexpr int CPR = SM::kCpr;
+    constexpr int RPI = SM::kRpi;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int per = (s_end - s_begin + W - 1) / W;
+    const int first = s_begin + wave * per;
+    const int niter = max(0, min(per, s_end - first));  // uniform per wave
+    if (niter == 0) return;
+    const int last = first + niter - 1;
+    // row of load l: RPI l + lane / CPR; X rows first (16), then A_k rank rows
+    const int c = lane % CPR;
+    const bf16_t *src[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        const int rho = RPI * l + lane / CPR;
+        src[l] = rho < kShrinkRows ? X + (size_t)rm(min(max(t0 + rho, lo), hi - 1)) * d_in
+                                   : Ak + (size_t)min(16 * NB * cg + rho - kShrinkRows, R - 1) * d_in;
+    }
+    uint4 *const buf = sm.stage[wave];
+
+    auto load = [&](ShrinkStage<NL> &st, int it) {
+        const int step = first + it;
+        const int e = min(step, last) * SM::kStepK + 8 * c;  // steps past the end reload the last step
+        const bool ok = step <= last && e < d_in;
+        const int ec = ok ? e : d_in - 8;                     // d_in >= 8: always inside the row
+        st.keep = ok ? ~0u : 0u;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) st.v[l] = ld16(src[l] + ec);
+    };
+    auto consume = [&](const ShrinkStage<NL> &st) {
+        // masked word by word: a select between whole vectors would make the
+        // compiler pick between their addresses and keep the ring in scratch
+        const uint32_t k = st.keep;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int rho = RPI * l + lane / CPR;
+            buf[rho * CPR + (c ^ (rho % CPR))] =
+                make_uint4(st.v[l].x & k, st.v[l].y & k, st.v[l].z & k, st.v[l].w & k);
+        }
+        const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int q = 0; q < SM::kStepK / 32; ++q) {
+            const int ch = 4 * q + g;
+            const bf16x8_t xo = as_bf16x8(buf[i * CPR + (ch ^ (i % CPR))]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int rho = kShrinkRows + 16 * b + i;
+                acc[b] = mfma_bf16(xo, as_bf16x8(buf[rho * CPR + (ch ^ (rho % CPR))]), acc[b]);
+            }
+        }
+    };
+
+    // The memory counter retires loads in issue order: scheduling barriers
+    // keep each step's loads together, so staging the oldest step waits for
+    // that step only.
+    ShrinkStage<NL> ring[S];
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) {
+        load(ring[u], u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int it0 = 0; it0 < niter; it0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            load(ring[(u + S - 1) % S], it0 + u + S - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(ring[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The whole workgroup: the tile's result for one piece (rows lo .. hi - 1,
+// adapter Ak) and column group cg, summed over the waves' partials in wave
+// order. On return, thread f < kNBW * 64 holds fragment f = 64 b + lane
+// (rows t0 + 4 g + v, column 16 (kNBW cg + b) + i, with g, i from lane) in
+// res for the rows of the piece; other rows of res are left as they were.
+// Ends with the LDS free again.
+template <int R, typename RM>
+__device__ __forceinline__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *Ak, int d_in, int t0, int lo,
+                                                 int hi, int cg, int s_begin, int s_end, ShrinkSmem<R> &sm,
+                                                 f32x4_t &res, RM rm) {
+    constexpr int NB = ShrinkSmem<R>::kNBW;
+    constexpr int W = ShrinkSmem<R>::kWaves;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    f32x4_t acc[NB];
+    shrink_wave_mfma<R>(X, Ak, d_in, t0, lo, hi, cg, s_begin, s_end, sm, acc, rm);
+    __syncthreads();  // every wave is done with its staging buffer, which the partials reuse
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sm.part[wave][b][lane] = acc[b];
+    __syncthreads();
+    const int f = threadIdx.x;
+    if (f < NB * kWave) {
+        f32x4_t sum = sm.part[0][f / kWave][f % kWave];
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum += sm.part[w][f / kWave][f % kWave];
+        const int g = (f % kWave) >> 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = t0 + 4 * g + v;
+            if (m >= lo && m < hi) res[v] = sum[v];
+        }
+    }
+    __syncthreads();
+}
+
+// ----------------------------------------------------------------------------
+// 64-row shrink tile (batches of many tiles, such as prefill): V[m, 0:R] =
+// X[m, :] . A_k for the rows m of up to two pieces
 // (segments, each with its own adapter) of the 64-row tile starting at t0,
 // over macro steps [ms_begin, ms_end) of d_in (kMacroK elements each). Wave w
 // owns rows t0 + 16 w .. + 15 and all R columns, so the waves share the A_k
@@ -236,13 +430,13 @@ __device__ void gather_pieces(PieceList &pl, const SegPrefetch &pre, const int32
 // c ^ (j % 16). The 16 lanes that read one chunk index from 16 different rows
 // then hit 16 different slots, i.e. different banks.
 // ----------------------------------------------------------------------------
-constexpr int kShrinkTileRows = 64;
+constexpr int kShrinkTileRows = 64;   // rows of a 64-row shrink tile (batches of many tiles)
 constexpr int kMacroK = 128;
 constexpr int kChunksPerRow = kMacroK * 2 / 16;   // 16-byte chunks per A_k row of a macro step
 constexpr int kPassPieces = 2;                    // pieces one pass over d_in can take
 
 template <int R>
-struct ShrinkSmem {
+struct Shrink64Smem {
     static constexpr int kNB = R < 16 ? 1 : R / 16;                   // 16-column MFMA blocks
     static constexpr int kALoads = R * kChunksPerRow < kBlockThreads ? 1 : R * kChunksPerRow / kBlockThreads;
     static constexpr int kStages = R >= 64 ? 2 : (R >= 32 ? 3 : 4);   // macro steps in flight
@@ -250,8 +444,8 @@ struct ShrinkSmem {
 };
 
 template <int R, int NP>
-struct ShrinkStage {
-    uint4 a[NP][ShrinkSmem<R>::kALoads];  // this thread's A_k chunks, per piece
+struct Shrink64Stage {
+    uint4 a[NP][Shrink64Smem<R>::kALoads];  // this thread's A_k chunks, per piece
     uint4 x[4];                           // this lane's X elements, slices 0..3
     uint32_t ok;                          // bits 0..3: X slice inside d_in; bits 4..: A chunk inside d_in
 };
@@ -262,12 +456,12 @@ struct ShrinkStage {
 // D layout) wherever that row lies in a piece; elsewhere res is left as it
 // was.
 template <int R, int NP, typename RM>
-__device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP], int d_in, int t0,
+__device__ void shrink_tile64_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP], int d_in, int t0,
                                  const int (&lo)[NP], const int (&hi)[NP], int ms_begin, int ms_end,
-                                 ShrinkSmem<R> &sm, f32x4_t (&res)[ShrinkSmem<R>::kNB], RM rm) {
-    constexpr int NB = ShrinkSmem<R>::kNB;
-    constexpr int kALoads = ShrinkSmem<R>::kALoads;
-    constexpr int S = ShrinkSmem<R>::kStages;
+                                 Shrink64Smem<R> &sm, f32x4_t (&res)[Shrink64Smem<R>::kNB], RM rm) {
+    constexpr int NB = Shrink64Smem<R>::kNB;
+    constexpr int kALoads = Shrink64Smem<R>::kALoads;
+    constexpr int S = Shrink64Smem<R>::kStages;
     constexpr int kAChunks = R * kChunksPerRow;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -291,7 +485,7 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP],
     // flight until its turn.
     const int niter = (ms_end - ms_begin + S - 1) / S * S;
 
-    auto load = [&](ShrinkStage<R, NP> &st, int it) {
+    auto load = [&](Shrink64Stage<R, NP> &st, int it) {
         const int ms = ms_begin + it;
         const bool step_ok = ms < ms_end;
         const int kb = max(0, min(ms, ms_end - 1)) * kMacroK;  // an empty range loads step 0
@@ -323,7 +517,7 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP],
 
     // Consume one stage: its A_k chunks go to LDS buffer `buf`, then every
     // wave multiplies its X slices with the chunk of each piece it touches.
-    auto consume = [&](const ShrinkStage<R, NP> &st, int buf) {
+    auto consume = [&](const Shrink64Stage<R, NP> &st, int buf) {
 #pragma unroll
         for (int u = 0; u < kALoads; ++u) {
             const int id = u * kBlockThreads + tid;
@@ -370,7 +564,7 @@ __device__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP],
     // The memory counter retires loads in issue order: scheduling barriers
     // keep each step's group of loads together, so consuming the oldest
     // group waits for that group only.
-    ShrinkStage<R, NP> ring[S];
+    Shrink64Stage<R, NP> ring[S];
 #pragma unroll
     for (int u = 0; u < S - 1; ++u) {
         load(ring[u], u);
@@ -459,7 +653,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // rm(p, ok): the row of Y that segment row p updates (never stored if !ok).
 template <int R, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready,
           typename RM>
-__device__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, float scale,
+__device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, float scale,
                                  ExpandSmem<R> &sm, const PieceList &pl, Gather gather, BkOf bk_of,
                                  LoadV4 load_v4, Ready ready, RM rm) {
     constexpr int K = ExpandSmem<R>::kK;

@@ -131,13 +131,14 @@ def test_fused_workspace_checks():
 
 
 def test_shrink_workspace_checks():
-    # a bf16 batch with few rows splits d_in between workgroups: workspace needed
-    need = sg.lib.sgmv_workspace_bytes(1, 64, 4096, 4096, 16, 1)
-    assert need > 4 * 64 * 16
-    assert shrink(M=64, d_in=4096, ws=None, wsb=0) == -6
-    # 4 tiles of 16 rows, d_in split 2 ways: 4 x 2 x 16 x 16 fp32 of partials alone
-    assert shrink(M=64, d_in=4096, wsb=4 * 2 * 16 * 16 * 4 - 1) == -6
-    assert shrink(M=64, d_in=4096, ws=0x800000 + 16, wsb=need) == -6
+    # one 16-row bf16 tile with a very long reduction (d_in = 28672, r = 64)
+    # splits d_in between workgroups: a workspace is needed
+    need = sg.lib.sgmv_workspace_bytes(1, 16, 28672, 4096, 64, 1)
+    assert need > 2 * 16 * 64 * 4
+    assert shrink(M=16, d_in=28672, r=64, ws=None, wsb=0) == -6
+    # the parts' partial tiles alone (16 x 64 fp32 each) exceed 4 KB
+    assert shrink(M=16, d_in=28672, r=64, wsb=4096) == -6
+    assert shrink(M=16, d_in=28672, r=64, ws=0x800000 + 16, wsb=need) == -6
     # fp32 never needs one (no MFMA path): NULL is fine; argument errors still win
     assert shrink(M=64, d_in=4096, dt=0, ws=None, wsb=0, r=12) == -3
 

@@ -24,6 +24,14 @@
  * dtype        SGMV_F32 or SGMV_BF16. X, Y and every adapter share it. V is
  *              always fp32. Arithmetic accumulates in fp32; Y is rounded once,
  *              to nearest-even, when stored.
+ * precision    bf16 segments of 16 rows or more expand on matrix cores, where
+ *              each fp32 V value enters as the sum of two bf16 values,
+ *              hi = rne(v) and lo = rne(v - hi): 16 significant bits, a
+ *              relative error of at most 2^-16 per value (exact for integer
+ *              V with |V| < 2^16). The expand error of such a row is then at
+ *              most (alpha / r) * 2^-16 * sum_j |V[m, j]| |B_k(j, n)| beyond
+ *              fp32 accumulation and the final rounding. Every other product
+ *              takes its operands exactly.
  * X            device, row-major M x d_in, contiguous, 16-byte aligned.
  * Y            device, row-major M x d_out, contiguous, 16-byte aligned;
  *              read and written (the delta is added to what Y holds).

@@ -656,10 +656,11 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
 // ----------------------------------------------------------------------------
 // Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready, typename RM>
+template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready, typename Commit,
+          typename RM>
 __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
                                             int nrows, int n0, bool active, float scale, Ready ready,
-                                            RM rm, const WaitCtl &wc) {
+                                            Commit commit, RM rm, const WaitCtl &wc) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     // Loads are unconditional (see shrink_wave): an inactive lane reads
@@ -718,7 +719,7 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
             }
         }
     }
-    if (!active) return;
+    if (!active || !commit()) return;
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
         if (m < nrows && yok[m]) {
@@ -734,33 +735,40 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
 
 // `bk_fn()` returns the address of the segment's B_k. `ready()` is called
 // (uniformly, possibly more than once) after B and Y have been requested and
-// before V is read; the rows are left untouched if it returns false. Rows
+// before V is read; the rows are left untouched if it returns false, or if
+// `commit()`, called (uniformly) once V is read and before Y is stored,
+// does. Rows
 // are taken kMaxRB (4 or 8) at a time: 8 reads B_k half as often, 4 needs
 // about 80 fewer registers per lane.
-template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready, typename RM>
+template <typename T, int R, bool kFlagged, int kMaxRB, typename BkFn, typename Ready, typename Commit,
+          typename RM>
 __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn, int d_out, int lo,
                                                int hi, int n0, bool active, float scale, Ready ready,
-                                               RM rm, const WaitCtl &wc) {
+                                               Commit commit, RM rm, const WaitCtl &wc) {
     static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
     for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
         const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
+            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
+                                           rm, wc);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
+            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
+                                           rm, wc);
         else if (kMaxRB == 4 || nrows <= 4)
-            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
+            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
+                                           rm, wc);
         else if constexpr (kMaxRB == 8)
-            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, rm, wc);
+            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
+                                           rm, wc);
     }
 }
 
 // One vector-path expand item: columns n0 .. n0 + VEC - 1 (per thread) of
 // segment s; `ready` as for expand_segment. Returns false if the segment is
 // empty, names no valid adapter or belongs to the MFMA path. In the fused
-// launch (kFlagged) a non-zero workspace status, checked once B and Y are
-// requested and before V is read, leaves its rows untouched (and returns
-// false). lo, hi receive the segment's rows.
+// launch (kFlagged) a non-zero workspace status as the launch began leaves
+// its rows untouched (and returns false). lo, hi receive the segment's
+// rows.
 template <typename T, int R, bool kFlagged, int kMaxRB, bool kSpec, typename ReadyFn, typename RM>
 __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const uint64_t *B_ptrs,
                                                    int num_adapters, const int32_t *seg_start,
@@ -774,14 +782,17 @@ __device__ __forceinline__ bool expand_vector_item(T *Y, const float *V, const u
     if (!vector_segment<T>(lo, hi, k, num_adapters)) return false;
     auto bk = [&]() { return reinterpret_cast<const T *>(tab.address(B_ptrs, k)); };
     if constexpr (kFlagged) {
-        // requested after the metadata: loads complete in order, so waiting
-        // for the metadata does not wait for it too
+        // Requested after the metadata (loads complete in order, so waiting
+        // for the metadata does not wait for it too) and looked at only
+        // before Y is stored, so that V is polled without waiting for it.
+        // On a failed workspace the polls end early (see give_up).
         const uint32_t st = read_status(wc);
-        auto ready_ok = [st, &ready]() { return st == 0 && ready(); };
-        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready_ok, rm, wc);
+        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready,
+                                               [st]() { return st == 0; }, rm, wc);
         return st == 0;
     } else {
-        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready, rm, wc);
+        expand_segment<T, R, kFlagged, kMaxRB>(Y, V, bk, d_out, lo, hi, n0, n0 < d_out, scale, ready,
+                                               []() { return true; }, rm, wc);
         return true;
     }
 }

@@ -62,6 +62,17 @@ def oracle_run(orc, w: wl.Workload):
     return V, Y
 
 
+def compact_rows(w: wl.Workload, c: DeviceCase) -> wl.Workload:
+    """w with its pools cut down to the slots its segments name, copied back
+    from the device (each segment then names its own slot): the oracle's
+    input for pools too large to hold on the host. Every row is kept."""
+    ids = np.asarray(w.seg_adapter, np.int64)
+    idx = torch.from_numpy(ids).to(c.A_pool.device)
+    return wl.Workload(w.name, w.M, w.d_in, w.d_out, w.r, w.alpha, w.dtype, len(ids), w.seg_start,
+                       np.arange(len(ids), dtype=np.int32), X=w.X, Y=w.Y,
+                       A_pool=c.A_pool[idx].cpu(), B_pool=c.B_pool[idx].cpu())
+
+
 def max_rel_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
     g = gpu.detach().cpu().to(torch.float64).numpy()
     err = np.abs(g - ref) / (1.0 + np.abs(ref))

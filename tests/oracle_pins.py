@@ -188,18 +188,20 @@ def pin_permutation(orc):
         assert np.array_equal(got2, got[rows])
 
 
-def signature_inputs(seg_start, seg_adapter, num_adapters, d_in, d_out, r, mode, dtype=torch.bfloat16):
+def signature_inputs(seg_start, seg_adapter, num_adapters, d_in, d_out, r, mode, dtype=torch.bfloat16,
+                     pool_device=None):
     """Weights that write each row's adapter id into columns 0..3 of its output.
 
     X[:, 0] = 1 and every other X is 0; alpha = r (scale 1); Y_in = 0. Base-16
     digit c of the id, plus one, lands in column c. Mode "A" encodes the id in
-    A (B is an identity block), mode "B" in B (A picks X[:, 0])."""
+    A (B is an identity block), mode "B" in B (A picks X[:, 0]). The pools are
+    built on `pool_device` (default: the host)."""
     M = int(seg_start[-1])
     X = torch.zeros((M, d_in), dtype=dtype)
     X[:, 0] = 1
-    A = torch.zeros((num_adapters, r, d_in), dtype=dtype)
-    B = torch.zeros((num_adapters, r, d_out), dtype=dtype)
-    ids = torch.arange(num_adapters)
+    A = torch.zeros((num_adapters, r, d_in), dtype=dtype, device=pool_device)
+    B = torch.zeros((num_adapters, r, d_out), dtype=dtype, device=pool_device)
+    ids = torch.arange(num_adapters, device=pool_device)
     digits = torch.stack([(ids >> (4 * c)) & 15 for c in range(4)], dim=1) + 1  # P x 4
     if mode == "A":
         A[:, :4, 0] = digits.to(dtype)

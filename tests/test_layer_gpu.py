@@ -9,7 +9,7 @@ import torch
 import segmented_gather_gemm_sgmv_amd as sg
 
 from . import workloads as wl
-from .gpu_common import assert_close, oracle_run, oracle_run_gather, rows_tensor, to_device
+from .gpu_common import assert_close, compact_rows, oracle_run, oracle_run_gather, rows_tensor, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -97,32 +97,22 @@ def test_layer_max_projections_and_workspace_reuse(dev, oracle):
 @pytest.mark.parametrize("name", ["slice70b", "layer7b"])
 def test_layer_whole_layers(dev, oracle, name):
     """A whole layer at full size, all 7 projections in one launch: the 70B
-    slice (checked against the oracle on 24 sampled rows per projection) and
-    the 7B decode layer (every row); bit for bit against the single calls."""
-    rng = np.random.Generator(np.random.PCG64(77))
-    if name == "slice70b":
-        ws = wl.slice70b()
-        rows = np.array(sorted(set([0, 511]) | set(rng.choice(512, size=22, replace=False).tolist())), np.int64)
-    else:
-        ws = wl.layer7b()
-        rows = np.arange(ws[0].M, dtype=np.int64)
+    slice (pools of 2000 adapters, 10.35 GB) and the 7B decode layer, every
+    row of every projection against the oracle (on the slots the rows name,
+    copied back one projection at a time), and bit for bit against the
+    single calls."""
+    ws = wl.slice70b() if name == "slice70b" else wl.layer7b()
     cs = []
     for w in ws:
         A = wl.device_pool(w.num_adapters, w.r, w.d_in, w.d_in ** -0.5, w.seed + 1, dev)
         B = wl.device_pool(w.num_adapters, w.r, w.d_out, w.r ** -0.5, w.seed + 2, dev)
         cs.append(to_device(w, dev, A_pool=A, B_pool=B))
     Ys = run_layer(cs)
-    r_t = torch.from_numpy(rows).to(dev)
     for w, c, Y in zip(ws, cs, Ys):
         assert torch.equal(Y, run_single(c)), f"{w.name}: layer call differs from the single call"
-        ids = w.seg_adapter[rows]
-        sub = wl.Workload(w.name, len(rows), w.d_in, w.d_out, w.r, w.alpha, w.dtype, len(rows),
-                          wl.segments_from_lengths([1] * len(rows)), np.arange(len(rows), dtype=np.int32),
-                          X=w.X[torch.from_numpy(rows)], Y=w.Y[torch.from_numpy(rows)],
-                          A_pool=c.A_pool[torch.from_numpy(ids).to(dev)].cpu(),
-                          B_pool=c.B_pool[torch.from_numpy(ids).to(dev)].cpu())
-        _, Y_ref = oracle_run(oracle, sub)
-        e = assert_close(Y[r_t], Y_ref, what=f"{w.name} layer")
-        print(f"{w.name}: layer max rel err {e:.2e}", flush=True)
-    del cs
+        _, Y_ref = oracle_run(oracle, compact_rows(w, c))
+        e = assert_close(Y, Y_ref, what=f"{w.name} layer")
+        print(f"{w.name}: layer max rel err {e:.2e} over {w.M} rows", flush=True)
+    del cs, Ys
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -13,8 +13,8 @@ import segmented_gather_gemm_sgmv_amd as sg
 
 from . import oracle_pins as pins
 from . import workloads as wl
-from .gpu_common import (TOL, assert_close, bits, oracle_bits, oracle_run, run_fused, run_split,
-                         to_device)
+from .gpu_common import (TOL, assert_close, bits, compact_rows, oracle_bits, oracle_run, run_fused,
+                         run_split, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,38 +54,82 @@ def test_config_parity(dev, oracle, name):
     print(f"{name}: max rel err V {ev:.2e}  Y {ey:.2e}  fused {ef:.2e}")
 
 
-def _slice70b_rows(M, count=24):
-    rng = np.random.Generator(np.random.PCG64(77))
-    rows = set([0, M - 1]) | set(rng.choice(M, size=count - 2, replace=False).tolist())
-    return np.array(sorted(rows), np.int64)
+def _free(*ts):
+    del ts
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def test_slice70b_parity(dev, oracle):
     """The 70B-layer slice at full size (512 rows, pools of 2000 adapters per
-    projection, 10.35 GB), checked on 24 sampled rows per projection."""
-    rows = _slice70b_rows(512)
+    projection, 10.35 GB in all), every row of every projection: V of the
+    split path, Y of the split and fused paths. One projection's pools are
+    on the device at a time; the 512 slots its rows name (at most 0.6 GB)
+    come back for the oracle."""
     for w in wl.slice70b():
         A = wl.device_pool(w.num_adapters, w.r, w.d_in, w.d_in ** -0.5, w.seed + 1, dev)
         B = wl.device_pool(w.num_adapters, w.r, w.d_out, w.r ** -0.5, w.seed + 2, dev)
         c = to_device(w, dev, A_pool=A, B_pool=B)
         V, Y = run_split(c)
         Yf = run_fused(c)
-        # oracle on the sampled rows: each is its own segment; only their
-        # adapters' slots are copied back
-        ids = w.seg_adapter[rows]
-        sub = wl.Workload(w.name, len(rows), w.d_in, w.d_out, w.r, w.alpha, w.dtype, len(rows),
-                          wl.segments_from_lengths([1] * len(rows)), np.arange(len(rows), dtype=np.int32),
-                          X=w.X[torch.from_numpy(rows)], Y=w.Y[torch.from_numpy(rows)],
-                          A_pool=A[torch.from_numpy(ids).to(dev)].cpu(),
-                          B_pool=B[torch.from_numpy(ids).to(dev)].cpu())
-        V_ref, Y_ref = oracle_run(oracle, sub)
-        r_t = torch.from_numpy(rows).to(dev)
-        ev = assert_close(V[r_t], V_ref, what=f"{w.name} V")
-        ey = assert_close(Y[r_t], Y_ref, what=f"{w.name} Y")
-        ef = assert_close(Yf[r_t], Y_ref, what=f"{w.name} fused Y")
-        print(f"{w.name}: max rel err V {ev:.2e}  Y {ey:.2e}  fused {ef:.2e}")
+        V_ref, Y_ref = oracle_run(oracle, compact_rows(w, c))
+        ev = assert_close(V, V_ref, what=f"{w.name} V")
+        ey = assert_close(Y, Y_ref, what=f"{w.name} Y")
+        ef = assert_close(Yf, Y_ref, what=f"{w.name} fused Y")
+        print(f"{w.name}: {w.M} rows, max rel err V {ev:.2e}  Y {ey:.2e}  fused {ef:.2e}", flush=True)
+        del A, B, c, V, Y, Yf
+        _free()
+
+
+def test_slice70b_integer_exact(dev, oracle):
+    """The 70B slice with integer values (X in -2..2, pools in -1..1, Y in
+    -8..8, alpha = 2r) on its 2000-slot pools: every partial sum is an exact
+    integer (|V| <= 2 * 28672 < 2^16), so V, split Y and fused Y equal the
+    oracle bit for bit on every row."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    for w in wl.slice70b():
+        w.X = torch.from_numpy(rng.integers(-2, 3, size=(w.M, w.d_in)).astype(np.float32)).to(w.dtype)
+        w.Y = torch.from_numpy(rng.integers(-8, 9, size=(w.M, w.d_out)).astype(np.float32)).to(w.dtype)
+        w.alpha = 2.0 * w.r
+        A = wl.device_int_pool(w.num_adapters, w.r, w.d_in, -1, 1, w.seed + 11, dev)
+        B = wl.device_int_pool(w.num_adapters, w.r, w.d_out, -1, 1, w.seed + 12, dev)
+        c = to_device(w, dev, A_pool=A, B_pool=B)
+        V, Y = run_split(c)
+        Yf = run_fused(c)
+        V_ref, Y_ref = oracle_run(oracle, compact_rows(w, c))
+        want = oracle_bits(oracle, Y_ref, w.dtype)
+        assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref), w.name
+        assert np.array_equal(bits(Y), want), w.name
+        assert np.array_equal(bits(Yf), want), w.name
+        print(f"{w.name}: bitwise on {w.M} rows", flush=True)
+        del A, B, c, V, Y, Yf
+        _free()
+
+
+@pytest.mark.parametrize("mode", ["A", "B"])
+def test_slice70b_indexing_signature(dev, oracle, mode):
+    """Adapter-id signatures through the 70B slice's 2000-slot pools (ids up
+    to 1999, three base-16 digits): every row's id comes back out of A (mode
+    A) or B (mode B), in both paths, and the oracle agrees on the slots the
+    rows name."""
+    for w in wl.slice70b():
+        X, A, B, alpha = pins.signature_inputs(w.seg_start, w.seg_adapter, w.num_adapters, w.d_in, w.d_out,
+                                               w.r, mode, dtype=w.dtype, pool_device=dev)
+        w.X, w.alpha = X, alpha
+        w.Y = torch.zeros((w.M, w.d_out), dtype=w.dtype)
+        c = to_device(w, dev, A_pool=A, B_pool=B)
+        want = pins.row_adapter(w.seg_start, w.seg_adapter, w.M)
+        for Y in (run_split(c)[1], run_fused(c)):
+            y = Y.cpu().to(torch.float64).numpy()
+            assert np.array_equal(pins.decode_signature(y), want), w.name
+            assert np.all(y[:, 4:] == 0), w.name
+        sub = compact_rows(w, c)
+        _, Y_ref = oracle_run(oracle, sub)
+        # the compacted pool numbers its slots 0..511: the oracle must find
+        # slot p's encoded id, the original one, on row p
+        assert np.array_equal(pins.decode_signature(Y_ref), want), w.name
         del A, B, c
-        torch.cuda.empty_cache()
+        _free()
 
 
 @pytest.mark.parametrize("name", CONFIGS)

@@ -193,6 +193,20 @@ def layer7b(seed: int = SEED_BASE + 6, M: int = 64, num_adapters: int = 256, r: 
     return out
 
 
+def device_int_pool(num_adapters: int, r: int, d: int, lo: int, hi: int, seed: int, device) -> torch.Tensor:
+    """A P x r x d bf16 pool of integers in lo..hi drawn on the device with a
+    seeded torch generator (integer_case's values for pools too large to
+    draw on the host)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    pool = torch.empty((num_adapters, r, d), dtype=torch.bfloat16, device=device)
+    chunk = max(1, (1 << 28) // (r * d))
+    for k0 in range(0, num_adapters, chunk):
+        k1 = min(num_adapters, k0 + chunk)
+        pool[k0:k1].copy_(torch.randint(lo, hi + 1, (k1 - k0, r, d), generator=g, device=device))
+    return pool
+
+
 def device_pool(num_adapters: int, r: int, d: int, std: float, seed: int, device) -> torch.Tensor:
     """A P x r x d bf16 pool drawn on the device with a seeded torch generator
     (for pools too large to draw on the host)."""

@@ -77,6 +77,36 @@ def profiled_traffic(workload, path, kernel):
     return None if k is None else k["traffic_bytes"]
 
 
+def profiled_mfma(workload):
+    """Per-kernel MfmaUtil (percent) from the committed rocprofv3 counter
+    summary for this workload (profiles/mfma_<workload>.md), or None when
+    there is none or the kernel sources have changed since it was taken."""
+    import re
+    from pathlib import Path
+    f = Path(ROOT) / "profiles" / f"mfma_{workload}.md"
+    if not f.exists():
+        return None
+    m = re.search(r"<!-- bench-mfma (\{.*\}) -->", f.read_text())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != sources_sha256():
+        return None
+    return rec.get("kernels")
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -88,7 +118,10 @@ def parse():
                    choices=["split", "fused", "split_gather", "fused_gather", "fused_permute", "fused_layer",
                             "per_segment"])
     p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB of touched bytes")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU-baseline leg (1 core, all cores)")
+    p.add_argument("--no-all-configs", action="store_true",
+                   help="skip the other workloads' summary (all_configs) in the default run")
+    p.add_argument("--config-steps", type=int, default=400, help="timed steps per path in all_configs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cold-calls", type=int, default=50,
                    help="calls timed one by one after writing 1 GiB, which evicts L2 and the Infinity Cache (0: skip)")
@@ -346,7 +379,7 @@ def cold_calls(reps, path, wsbuf, n):
             "p90_us": float(np.percentile(us, 90))}
 
 
-def hbm_probe(dev, workload_bytes):
+def hbm_probe(dev, workload_bytes, full=True):
     """What a plain streaming-read kernel (the library's stream probe) reaches
     on this GPU: over 4 GiB, and over the workload's own byte count (windows
     rotated over 1 GiB, so the Infinity Cache cannot serve them), best of a
@@ -371,14 +404,15 @@ def hbm_probe(dev, workload_bytes):
         return a.elapsed_time(b) * 1e3 / (reps * len(launches))   # us per launch
 
     out = {}
-    big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
-    best = None
-    for blocks in (256, 512, 1024, 2048, 4096):
-        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
-        us = timed([(big, big.numel(), sink)], 5)
-        best = us if best is None or us < best else best
-    out["GB_per_s_4GiB"] = big.numel() / (best * 1e-6) / 1e9
-    del big
+    if full:
+        big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        best = None
+        for blocks in (256, 512, 1024, 2048, 4096):
+            sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+            us = timed([(big, big.numel(), sink)], 5)
+            best = us if best is None or us < best else best
+        out["GB_per_s_4GiB"] = big.numel() / (best * 1e-6) / 1e9
+        del big
     n = (workload_bytes + 15) // 16 * 16
     windows = max(1, (1 << 30) // n)
     buf = torch.empty(windows * n, dtype=torch.uint8, device=dev)
@@ -390,6 +424,7 @@ def hbm_probe(dev, workload_bytes):
             best, best_blocks = us, blocks
     out.update({"bytes_at_workload_size": n, "us_at_workload_size": best, "blocks": best_blocks,
                 "GB_per_s_at_workload_size": n / (best * 1e-6) / 1e9})
+    del buf
     return out
 
 
@@ -459,9 +494,11 @@ def admission_times(dev, reps=40):
 
 
 def cpu_baseline(ws, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole batches of the first projection, repeated for about `seconds`."""
-    import torch
+    """The oracle (C, fp64 arithmetic), as it stands, on a bounded sample of
+    the same workload: whole batches of the first projection, repeated for
+    about `seconds`, once on one core (this thread pinned to one CPU, one
+    OpenMP thread) and once on all cores (the OpenMP default). Affinity and
+    thread count are restored afterwards."""
     import oracle
     from tests import workloads as wl
     orc = oracle.get()
@@ -476,21 +513,139 @@ def cpu_baseline(ws, seconds):
     else:
         A, B, seg_adapter = w.A_pool, w.B_pool, w.seg_adapter
     args = (wl.storage(w.Y), wl.storage(w.X), wl.storage(A), wl.storage(B), w.seg_start, seg_adapter, w.alpha)
-    orc.sgmv(*args)  # warm
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.sgmv(*args)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per_call = el / reps
     nbytes = w.algorithmic_bytes()
-    return {"value": nbytes / per_call / 1e9, "unit": "GB/s", "cores": oracle.threads_used(),
-            "kind": "oracle", "us_per_call": per_call * 1e6,
-            "sample": f"{reps} whole {w.name} batches ({w.M} rows, {w.num_segments} segments), "
-                      f"{el:.1f} s of CPU work"}
+
+    def leg():
+        orc.sgmv(*args)  # warm
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            orc.sgmv(*args)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per_call = el / reps
+        return {"value": nbytes / per_call / 1e9, "unit": "GB/s", "cores": oracle.threads_used(),
+                "us_per_call": per_call * 1e6, "calls": reps, "seconds": el}
+
+    all_cores = leg()
+    mask = os.sched_getaffinity(0)
+    old_threads = oracle.set_threads(1)
+    try:
+        os.sched_setaffinity(0, {min(mask)})
+        one_core = leg()
+    finally:
+        os.sched_setaffinity(0, mask)
+        oracle.set_threads(old_threads)
+    return {"value": all_cores["value"], "unit": "GB/s", "cores": all_cores["cores"], "kind": "oracle",
+            "precision": "fp64 (C loops, inputs widened exactly)", "cpu_model": cpu_model(),
+            "us_per_call": all_cores["us_per_call"],
+            "sample": f"whole {w.name} batches ({w.M} rows, {w.num_segments} segments, {nbytes} algorithmic "
+                      f"bytes each): {all_cores['calls']} calls in {all_cores['seconds']:.1f} s on "
+                      f"{all_cores['cores']} threads, {one_core['calls']} calls in {one_core['seconds']:.1f} s "
+                      f"on one core",
+            "all_cores": all_cores, "one_core": one_core}
+
+
+def workspace_for(ws, group, path, dev):
+    """One zero-filled workspace that serves every call of the path (calls
+    run in order on one stream and each leaves it zero)."""
+    import torch
+    import segmented_gather_gemm_sgmv_amd as sg
+    need = max(sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype) for w in ws)
+    if path == "fused_layer":
+        need = sg.sgmv_layer_workspace_bytes([(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs) for rp in group],
+                                             ws[0].num_segments, ws[0].M, ws[0].r, ws[0].dtype)
+    return torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+
+def timed_steps(reps, path, steps, warmup, wsbuf):
+    """Milliseconds per step: `warmup` untimed steps, then exactly `steps`
+    steps replayed from HIP graphs (one graph over all replicas, plus one for
+    the remainder), bracketed by events on the replay stream."""
+    import torch
+    R = len(reps)
+    for i in range(warmup):
+        step(reps[i % R], path, wsbuf)
+    torch.cuda.synchronize()
+    full = capture(reps, path, 0, R, wsbuf) if steps >= R else None
+    rem = steps % R if steps >= R else steps
+    tail = capture(reps, path, 0, rem, wsbuf) if rem else None
+    if full is not None:
+        full.replay()  # untimed replay: page in the graph
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps // R if full is not None else 0):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def launch_bytes(ws, path):
+    """Algorithmic bytes per launch of each kernel of the path, averaged over
+    the projections as the kernel timings average launches."""
+    if path == "fused_layer":  # one launch covers every projection
+        return {"fused_layer": sum(w.algorithmic_bytes() for w in ws)}
+    per_kernel = kernel_bytes(ws[0], path)
+    if len(ws) > 1:
+        for w in ws[1:]:
+            for n, b in kernel_bytes(w, path).items():
+                per_kernel[n] += b
+        per_kernel = {n: b / len(ws) for n, b in per_kernel.items()}
+    return per_kernel
+
+
+def config_summary(name, dev, steps, cold_n):
+    """One workload in brief, for the all_configs object: per path, the step
+    time, the rate and its fraction of the 8 TB/s peak, each kernel's
+    average duration and fraction, the HBM traffic over algorithmic bytes
+    from the committed counter summaries (None when stale), and the cold
+    median; then the rate over what a plain streaming read reaches at the
+    same byte count. Prefill adds its matrix-core figures."""
+    import torch
+    ws = make_workloads(name)
+    nbytes = sum(w.algorithmic_bytes() for w in ws)
+    R = max(1, min(256, -(-(1 << 30) // nbytes)))
+    reps = build_replicas(ws, dev, R)
+    out = {"algorithmic_bytes_per_step": nbytes, "projections": len(ws), "replicas": R,
+           "tokens": ws[0].M, "segments": ws[0].num_segments, "r": ws[0].r}
+    paths = ["fused", "split"] + (["fused_layer"] if len(ws) > 1 else [])
+    for path in paths:
+        wsbuf = workspace_for(ws, reps[0], path, dev)
+        ms = timed_steps(reps, path, steps, max(10, steps // 10), wsbuf)
+        kus = time_kernels(reps, path, steps, wsbuf)
+        kb = launch_bytes(ws, path)
+        rate = nbytes / (ms * 1e-3) / 1e9
+        rec = {"us_per_step": ms * 1e3, "GB_per_s": rate, "frac_of_peak": rate / HBM_PEAK_GBS,
+               "kernels_us": kus,
+               "kernel_frac_of_peak": {k: kb[k] / (kus[k] * 1e-6) / 1e9 / HBM_PEAK_GBS for k in kus},
+               "traffic_over_algorithmic": {}}
+        for k in kus:
+            t = profiled_traffic(name, path, k)
+            rec["traffic_over_algorithmic"][k] = None if t is None else t / kb[k]
+        if cold_n > 0:
+            rec["cold_median_us"] = cold_calls(reps, path, wsbuf, cold_n)["median_us"]
+        out[path] = rec
+        del wsbuf
+    probe = hbm_probe(dev, nbytes, full=False)
+    out["probe_GB_per_s_at_workload_size"] = probe["GB_per_s_at_workload_size"]
+    out["value_over_probe"] = out["fused"]["GB_per_s"] / probe["GB_per_s_at_workload_size"]
+    if name == "prefill":
+        flops = sum(w.flops() for w in ws)
+        us = out["fused"]["kernels_us"]["fused"]
+        out["mfma"] = {"algorithmic_TFLOP_per_s": flops / (us * 1e-6) / 1e12,
+                       "frac_of_2500_TFLOP_per_s": flops / (us * 1e-6) / 1e12 / 2500.0,
+                       "MfmaUtil_pct_profiled": profiled_mfma(name)}
+    del reps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -514,45 +669,12 @@ def main():
                 rp.segments
     torch.cuda.synchronize()
 
-    # one zero-filled workspace serves every fused call (they run in order on
-    # one stream and each returns the control words to zero)
-    need = max(sg.sgmv_workspace_bytes(w.num_segments, w.M, w.d_in, w.d_out, w.r, w.dtype) for w in ws)
-    if args.path == "fused_layer":
-        need = sg.sgmv_layer_workspace_bytes([(rp.Y, rp.X, rp.A_ptrs, rp.B_ptrs) for rp in reps[0]],
-                                             ws[0].num_segments, ws[0].M, ws[0].r, ws[0].dtype)
-    wsbuf = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-
-    for i in range(args.warmup):
-        step(reps[i % R], args.path, wsbuf)
-    torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps, replayed from HIP graphs (one graph
-    # over all R replicas, plus one for the remainder).
-    full = capture(reps, args.path, 0, R, wsbuf) if args.steps >= R else None
-    rem = args.steps % R if args.steps >= R else args.steps
-    tail = capture(reps, args.path, 0, rem, wsbuf) if rem else None
-    if full is not None:
-        full.replay()  # untimed replay: page in the graph
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps // R if full is not None else 0):
-        full.replay()
-    if tail is not None:
-        tail.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    wsbuf = workspace_for(ws, reps[0], args.path, dev)
+    ms = timed_steps(reps, args.path, args.steps, args.warmup, wsbuf)
 
     # per-kernel durations, for the roofline
     kus = time_kernels(reps, args.path, args.steps, wsbuf)
-    per_kernel = kernel_bytes(ws[0], args.path)
-    if args.path == "fused_layer":  # one launch covers every projection
-        per_kernel = {"fused_layer": sum(w.algorithmic_bytes() for w in ws)}
-    elif len(ws) > 1:  # several projections: average bytes per launch, as kus averages time
-        for w in ws[1:]:
-            for n, b in kernel_bytes(w, args.path).items():
-                per_kernel[n] += b
-        per_kernel = {n: b / len(ws) for n, b in per_kernel.items()}
+    per_kernel = launch_bytes(ws, args.path)
     dom = max(kus, key=kus.get)   # the kernel that takes the most time per step
     achieved = per_kernel[dom] / (kus[dom] * 1e-6) / 1e9
 
@@ -604,6 +726,11 @@ def main():
         out["hbm_probe"] = probe
     if args.admission:
         out["admission"] = admission_times(dev)
+    if args.workload == "decode_distinct" and args.path == "fused" and not args.no_all_configs:
+        del reps, wsbuf
+        torch.cuda.empty_cache()
+        out["all_configs"] = {name: config_summary(name, dev, args.config_steps, 20 if args.cold_calls else 0)
+                              for name in ("tiny", "decode_skewed", "prefill", "slice70b")}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)
     print(json.dumps(out), flush=True)

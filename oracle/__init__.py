@@ -228,9 +228,16 @@ def get() -> Oracle:
 
 
 def threads_used() -> int:
-    """OpenMP threads the oracle's loops run on (OMP_NUM_THREADS, else all CPUs
-    of this process's affinity mask)."""
-    env = os.environ.get("OMP_NUM_THREADS")
-    if env and env.strip().isdigit():
-        return int(env)
-    return len(os.sched_getaffinity(0))
+    """OpenMP threads the oracle's loops run on now (the OpenMP runtime the
+    oracle library is linked with: OMP_NUM_THREADS, else all CPUs of this
+    process's affinity mask, unless set_threads changed it)."""
+    return int(get().lib.omp_get_max_threads())
+
+
+def set_threads(n: int) -> int:
+    """Run the oracle's loops on n OpenMP threads from now on; returns the
+    previous count."""
+    lib = get().lib
+    old = int(lib.omp_get_max_threads())
+    lib.omp_set_num_threads(int(n))
+    return old

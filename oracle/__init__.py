@@ -220,10 +220,12 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
-    """The oracle built from ``sgmv_oracle.c`` (compiled on first use)."""
+    """The oracle built from ``sgmv_oracle.c`` (compiled on first use), or
+    the build named by the environment variable SGMV_ORACLE_LIBRARY (the
+    tests load a sanitizer build of the same source that way)."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("SGMV_ORACLE_LIBRARY") or LIBRARY)
     return _default
 
 

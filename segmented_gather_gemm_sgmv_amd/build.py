@@ -1,6 +1,6 @@
 """Build libsgmv.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m segmented_gather_gemm_sgmv_amd.build``.
+Usage: ``python segmented_gather_gemm_sgmv_amd/build.py``.
 
 The kernel file is compiled once per rank (-DSGMV_RANK=8, 16, 32, 64) and
 once more for the rank dispatch and helper kernels; these objects and the
@@ -23,7 +23,8 @@ LIBRARY = PKG / "libsgmv.so"
 
 KERNELS = CSRC / "sgmv_kernels.hip"
 API = CSRC / "sgmv_api.cpp"
-SOURCES = [KERNELS, API]
+HOST = CSRC / "sgmv_host.cpp"  # host-only entry points (no HIP): also built alone with the sanitizers
+SOURCES = [KERNELS, API, HOST]
 RANKS = (8, 16, 32, 64)
 ARCH = "gfx950"
 
@@ -53,7 +54,8 @@ def build(output: Path = LIBRARY, extra_flags=(), verbose: bool = False, jobs: i
     jobs = jobs or min(8, os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="sgmv_build_") as tmp:
         units = [(KERNELS, [f"-DSGMV_RANK={r}"], Path(tmp) / f"kernels_r{r}.o") for r in RANKS]
-        units += [(KERNELS, [], Path(tmp) / "kernels_dispatch.o"), (API, [], Path(tmp) / "api.o")]
+        units += [(KERNELS, [], Path(tmp) / "kernels_dispatch.o"), (API, [], Path(tmp) / "api.o"),
+                  (HOST, [], Path(tmp) / "host.o")]
         pending = list(units)
         running = []
         failed = []

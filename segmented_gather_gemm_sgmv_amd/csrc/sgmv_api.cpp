@@ -1,83 +1,25 @@
-// The C ABI declared in include/sgmv.h: argument checks, dispatch to the
-// gfx950 kernels, and the host-side metadata helpers.
+// The launching entry points of the C ABI declared in include/sgmv.h:
+// argument checks, then dispatch to the gfx950 kernels. The host-only entry
+// points (size queries, metadata helpers) are in sgmv_host.cpp.
 #include "sgmv.h"
 
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
-#include <numeric>
-#include <vector>
-
+#include "sgmv_checks.h"
 #include "sgmv_launch.h"
 
-static_assert(SGMV_NOALLOC_SCRATCH_BYTES == sgmv::kScratchBytes, "scratch size of the header and the library agree");
-static_assert(SGMV_WS_WAIT_TIMEOUT == sgmv::kStatusTimeout && SGMV_WS_BAD_OFFSETS == sgmv::kStatusBadOffsets,
-              "status bits of the header and the kernels agree");
+using namespace sgmv::abi;
 
 namespace {
-
-bool valid_rank(int32_t r) { return r == 8 || r == 16 || r == 32 || r == 64; }
-bool valid_dtype(int32_t dt) { return dt == SGMV_F32 || dt == SGMV_BF16; }
-bool valid_dim(int32_t d) { return d > 0 && d % 8 == 0; }
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Largest element count one operand may span: indices are formed in 64-bit
-// arithmetic, but a segment's row count and a column index stay in int.
-constexpr int64_t kMaxElems = (int64_t)1 << 40;
-
-int check_common(int32_t num_adapters, int32_t num_segments, int32_t M, int32_t r,
-                 int32_t dtype) {
-    if (!valid_dtype(dtype)) return SGMV_ERR_DTYPE;
-    if (!valid_rank(r)) return SGMV_ERR_RANK;
-    if (M < 0 || num_segments < 0 || num_adapters < 0) return SGMV_ERR_SHAPE;
-    return SGMV_OK;
-}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int sgmv_version(void) { return 300; }
-
-const char *sgmv_status_string(int status) {
-    switch (status) {
-        case SGMV_OK: return "ok";
-        case SGMV_ERR_NULL: return "a required pointer is NULL";
-        case SGMV_ERR_SHAPE: return "invalid size (negative, not a multiple of 8, or too large)";
-        case SGMV_ERR_RANK: return "rank must be 8, 16, 32 or 64";
-        case SGMV_ERR_DTYPE: return "dtype must be SGMV_F32 or SGMV_BF16";
-        case SGMV_ERR_ALIGN: return "X, Y and V must be 16-byte aligned";
-        case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
-        case SGMV_ERR_HIP: return "HIP runtime error at launch";
-        case SGMV_ERR_ADAPTER: return "adapter id negative or outside the pool";
-        case SGMV_ERR_SCRATCH: return "batch needs more workspace than the library's static scratch holds";
-        default: return "unknown status";
-    }
-}
-
-size_t sgmv_workspace_bytes(int32_t num_segments, int32_t M, int32_t d_in, int32_t d_out,
-                            int32_t r, int32_t dtype) {
-    if (num_segments < 0 || M < 0 || !valid_dim(d_in) || !valid_dim(d_out) || !valid_rank(r) ||
-        !valid_dtype(dtype))
-        return 0;
-    return std::max(sgmv::shrink_layout(M, d_in, r, dtype).total,
-                    sgmv::fused_layout(M, d_in, d_out, r, dtype).total);
-}
-
-namespace {
 int check_workspace(const void *workspace, size_t workspace_bytes, size_t need) {
     if (need == 0) return SGMV_OK;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
         return SGMV_ERR_WORKSPACE;
     return SGMV_OK;
 }
-}  // namespace
-
-}  // extern "C"
-
-namespace {
 
 // The checks and launches shared by the contiguous calls (rows == NULL,
 // gathered == false) and the gathered ones (rows required when M > 0).
@@ -87,7 +29,8 @@ int shrink_call(float *V, const void *X, const int32_t *rows, bool gathered, con
                 size_t workspace_bytes, void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
-    if (!valid_dim(d_in) || (int64_t)M * d_in > kMaxElems) return SGMV_ERR_SHAPE;
+    st = check_sizes(M, num_segments, d_in, 8, r, dtype);
+    if (st != SGMV_OK) return st;
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!V || !X || !A_ptrs || !seg_start || !seg_adapter || (gathered && !rows)) return SGMV_ERR_NULL;
     if (!aligned16(V) || !aligned16(X)) return SGMV_ERR_ALIGN;
@@ -104,7 +47,8 @@ int expand_call(void *Y, const float *V, const int32_t *rows, bool gathered, con
                 void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
-    if (!valid_dim(d_out) || (int64_t)M * d_out > kMaxElems) return SGMV_ERR_SHAPE;
+    st = check_sizes(M, num_segments, 8, d_out, r, dtype);
+    if (st != SGMV_OK) return st;
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!Y || !V || !B_ptrs || !seg_start || !seg_adapter || (gathered && !rows)) return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(V)) return SGMV_ERR_ALIGN;
@@ -120,9 +64,8 @@ int fused_call(void *Y, const void *X, const int32_t *rows, bool gathered, const
                void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
-    if (!valid_dim(d_in) || !valid_dim(d_out) || (int64_t)M * d_in > kMaxElems ||
-        (int64_t)M * d_out > kMaxElems)
-        return SGMV_ERR_SHAPE;
+    st = check_sizes(M, num_segments, d_in, d_out, r, dtype);
+    if (st != SGMV_OK) return st;
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter || (gathered && !rows))
         return SGMV_ERR_NULL;
@@ -143,9 +86,8 @@ int fused_noalloc_call(void *Y, const void *X, const uint64_t *A_ptrs, const uin
                        int32_t dtype, void *stream) {
     int st = check_common(num_adapters, num_segments, M, r, dtype);
     if (st != SGMV_OK) return st;
-    if (!valid_dim(d_in) || !valid_dim(d_out) || (int64_t)M * d_in > kMaxElems ||
-        (int64_t)M * d_out > kMaxElems)
-        return SGMV_ERR_SHAPE;
+    st = check_sizes(M, num_segments, d_in, d_out, r, dtype);
+    if (st != SGMV_OK) return st;
     if (M == 0 || num_segments == 0) return SGMV_OK;
     if (!Y || !X || !A_ptrs || !B_ptrs || !seg_start || !seg_adapter) return SGMV_ERR_NULL;
     if (!aligned16(Y) || !aligned16(X)) return SGMV_ERR_ALIGN;
@@ -216,39 +158,6 @@ int sgmv_fused_gather(void *Y, const void *X, const int32_t *rows, const uint64_
                       num_segments, M, d_in, d_out, r, alpha, dtype, workspace, workspace_bytes, stream);
 }
 
-}  // extern "C"
-
-namespace {
-
-// Copies and checks the host descriptors; SGMV_OK and *count = 0 when there is
-// nothing to do.
-int layer_inputs(const sgmv_projection *projections, int32_t num_projections, int32_t num_segments, int32_t M,
-                 int32_t r, int32_t dtype, sgmv::LayerProjIn *out) {
-    if (num_projections < 0 || num_projections > SGMV_MAX_PROJECTIONS) return SGMV_ERR_SHAPE;
-    if (num_projections > 0 && !projections) return SGMV_ERR_NULL;
-    for (int32_t q = 0; q < num_projections; ++q) {
-        const sgmv_projection &p = projections[q];
-        int st = check_common(p.num_adapters, num_segments, M, r, dtype);
-        if (st != SGMV_OK) return st;
-        if (!valid_dim(p.d_in) || !valid_dim(p.d_out) || (int64_t)M * p.d_in > kMaxElems ||
-            (int64_t)M * p.d_out > kMaxElems)
-            return SGMV_ERR_SHAPE;
-        out[q] = sgmv::LayerProjIn{p.Y, p.X, p.A_ptrs, p.B_ptrs, p.num_adapters, p.d_in, p.d_out};
-    }
-    return SGMV_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-size_t sgmv_layer_workspace_bytes(const sgmv_projection *projections, int32_t num_projections,
-                                  int32_t num_segments, int32_t M, int32_t r, int32_t dtype) {
-    sgmv::LayerProjIn in[sgmv::kMaxProjections];
-    if (layer_inputs(projections, num_projections, num_segments, M, r, dtype, in) != SGMV_OK) return 0;
-    return sgmv::layer_workspace_total(in, num_projections, num_segments, M, r, dtype);
-}
-
 int sgmv_fused_layer(const sgmv_projection *projections, int32_t num_projections, const int32_t *rows,
                      const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments, int32_t M,
                      int32_t r, float alpha, int32_t dtype, void *workspace, size_t workspace_bytes,
@@ -282,30 +191,6 @@ int sgmv_fused_layer(const sgmv_projection *projections, int32_t num_projections
     return hip_status(sgmv::launch_fused_layer(a, static_cast<hipStream_t>(stream)));
 }
 
-int sgmv_build_segments(const int32_t *token_adapter, int32_t M, int32_t *perm,
-                        int32_t *seg_start, int32_t *seg_adapter, int32_t *num_segments) {
-    if (M < 0) return SGMV_ERR_SHAPE;
-    if (!num_segments || !seg_start || (M > 0 && (!token_adapter || !perm || !seg_adapter)))
-        return SGMV_ERR_NULL;
-    for (int32_t i = 0; i < M; ++i)
-        if (token_adapter[i] < 0) return SGMV_ERR_ADAPTER;
-    std::iota(perm, perm + M, 0);
-    std::stable_sort(perm, perm + M, [token_adapter](int32_t a, int32_t b) {
-        return token_adapter[a] < token_adapter[b];
-    });
-    int32_t n = 0;
-    for (int32_t p = 0; p < M; ++p) {
-        const int32_t id = token_adapter[perm[p]];
-        if (p == 0 || id != token_adapter[perm[p - 1]]) {
-            seg_start[n] = p;
-            seg_adapter[n] = id;
-            ++n;
-        }
-    }
-    seg_start[n] = M;
-    *num_segments = n;
-    return SGMV_OK;
-}
 
 int sgmv_admit_adapter(void *A_slot, void *B_slot, const void *A_host, const void *B_host,
                        size_t A_bytes, size_t B_bytes, uint64_t *A_ptrs, uint64_t *B_ptrs,
@@ -339,27 +224,6 @@ int sgmv_workspace_status(const void *workspace, uint32_t *status, void *stream)
 
 uint32_t sgmv_set_wait_limit(uint32_t polls) { return sgmv::set_wait_limit(polls); }
 
-int sgmv_check_segments(const int32_t *seg_start, const int32_t *seg_adapter, int32_t num_segments,
-                        int32_t M, int32_t num_adapters) {
-    if (num_segments < 0 || M < 0 || num_adapters < 0) return SGMV_ERR_SHAPE;
-    if (!seg_start || (num_segments > 0 && !seg_adapter)) return SGMV_ERR_NULL;
-    if (seg_start[0] != 0 || seg_start[num_segments] != M) return SGMV_ERR_SHAPE;
-    for (int32_t s = 0; s < num_segments; ++s) {
-        if (seg_start[s + 1] < seg_start[s]) return SGMV_ERR_SHAPE;
-        if (seg_adapter[s] < 0 || seg_adapter[s] >= num_adapters) return SGMV_ERR_ADAPTER;
-    }
-    return SGMV_OK;
-}
 
-int sgmv_pool_pointers(uint64_t *ptrs_host, const void *base, int32_t num_adapters,
-                       int64_t slot_bytes) {
-    if (num_adapters < 0 || slot_bytes < 0) return SGMV_ERR_SHAPE;
-    if (num_adapters == 0) return SGMV_OK;
-    if (!ptrs_host || !base) return SGMV_ERR_NULL;
-    if ((slot_bytes & 15) != 0 || !aligned16(base)) return SGMV_ERR_ALIGN;
-    const uint64_t b = reinterpret_cast<uintptr_t>(base);
-    for (int32_t k = 0; k < num_adapters; ++k) ptrs_host[k] = b + (uint64_t)k * (uint64_t)slot_bytes;
-    return SGMV_OK;
-}
 
 }  // extern "C"

@@ -1125,6 +1125,8 @@ __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
 // ----------------------------------------------------------------------------
 static_assert(kTileRows64 == kTileRows && kShrinkRows16 == kShrinkRows,
               "workspace layouts must match the MFMA tiles");
+static_assert(kLaunchThreads == kBlock && kExpandCols == kExpandTileCols && kWavesPerBlock == 4 && kXcds == 8,
+              "launch sizes counted on the host must match the kernels");
 
 static int mfma_tiles(int dtype, int M) { return dtype == kBF16 ? (M + kTileRows - 1) / kTileRows : 0; }
 

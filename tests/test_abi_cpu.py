@@ -107,6 +107,21 @@ def test_argument_errors(call):
 
 
 @pytest.mark.parametrize("call", ALL_CALLS, ids=lambda f: f.__name__)
+def test_launches_beyond_the_dispatch_limit_are_refused(call):
+    """A call whose launch would need more than 2^24 workgroups (2^32
+    work-items in one dispatch) is refused before anything is enqueued:
+    2^24 segments of one row each, rank 64 (16 shrink workgroups per
+    segment). Half as many segments at rank 8 fit, and fail only the
+    later (pointer) check."""
+    big = dict(N=1 << 24, M=1 << 24)
+    assert call(**big, r=64) == -2
+    assert call(N=1 << 20, M=1 << 20, r=8, ss=None) == -1
+    if call in (fused, fused_gather):
+        assert sg.lib.sgmv_workspace_bytes(1 << 24, 1 << 24, 64, 64, 64, 1) == 0
+        assert sg.lib.sgmv_workspace_bytes(1 << 20, 1 << 20, 64, 64, 8, 1) > 0
+
+
+@pytest.mark.parametrize("call", ALL_CALLS, ids=lambda f: f.__name__)
 def test_empty_is_noop(call):
     # nothing to do: OK without touching any pointer, even NULL ones
     first = "V" if call in (shrink, shrink_gather) else "Y"

@@ -40,6 +40,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "sgmv_common.h"
 #include "sgmv_launch.h"
@@ -214,6 +215,108 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
     }
 }
 
+// Segments of kSplitRows rows or more take the shrink a workgroup at a
+// time: the four waves split d_in, and each covers a block of up to 4 rows
+// and the workgroup's four rank rows j0 .. j0 + 3. A wave then streams its
+// quarter of the block's X rows and of the four A_k rows, so X crosses the
+// L1 once per workgroup instead of once per rank row, and a wave's loads
+// fit in flight at once (d_in = 4096: two 16-byte vectors per lane and
+// row). The partial sums meet in LDS and are added in wave order. (Blocks
+// of 8 rows would halve the passes but cost the fused kernel its
+// occupancy.)
+constexpr int kSplitRows = 3;
+
+struct ShrinkSplitSmem {
+    float part[kWavesPerBlock][4 * kWavesPerBlock];  // [wave][row * 4 + rank row]
+};
+
+template <typename T, int R, int ROWS, bool kFlagged, typename RM>
+__device__ __forceinline__ void shrink_block_split(float *V, const T *X, const T *Ak, int d_in, int row0,
+                                                   int nrows, int j0, RM rm, int copies, size_t copy_stride,
+                                                   ShrinkSplitSmem &sm) {
+    constexpr int VEC = Elem<T>::kPerVec;
+    constexpr int J = kWavesPerBlock;
+    constexpr int NV = ROWS * J;
+    constexpr int U = 2;  // (ROWS + 4) * U vectors in flight per lane
+    static_assert(ROWS * J <= 4 * kWavesPerBlock, "one block's partial sums fit the LDS buffer");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nvec = d_in / VEC;
+    const int quarter = (nvec + J - 1) / J;
+    const int vbeg = wave * quarter, vend = min(nvec, vbeg + quarter);
+    float acc[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) acc[q] = 0.f;
+    const T *xrow[ROWS];
+#pragma unroll
+    for (int m = 0; m < ROWS; ++m) xrow[m] = X + (size_t)rm(row0 + min(m, nrows - 1)) * d_in;
+    // Loads are unconditional: a vector past the wave's range reads a clamped
+    // address and is zeroed; rows past the block repeat its last row and are
+    // never stored.
+    for (int base = vbeg; base < vend; base += kWave * U) {
+        uint4 x[ROWS][U], a[J][U];
+        bool ok[U];
+        int vc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = base + u * kWave + lane;
+            ok[u] = v < vend;
+            vc[u] = ok[u] ? v : vend - 1;
+        }
+#pragma unroll
+        for (int m = 0; m < ROWS; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[m][u] = ld16(xrow[m] + (size_t)vc[u] * VEC);
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[jj][u] = ld16_stream(Ak + (size_t)(j0 + jj) * d_in + (size_t)vc[u] * VEC);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int jj = 0; jj < J; ++jj) {
+                if (!ok[u]) a[jj][u] = make_uint4(0, 0, 0, 0);
+                float af[VEC];
+                widen<T>(a[jj][u], af);
+#pragma unroll
+                for (int m = 0; m < ROWS; ++m) {
+                    float xf[VEC];
+                    widen<T>(x[m][u], xf);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[m * J + jj] = fmaf(xf[e], af[e], acc[m * J + jj]);
+                }
+            }
+        }
+    }
+    wave_reduce_transpose<NV>(acc, lane);
+    constexpr int kSpread = kWave / NV;  // lanes holding the same value's total
+    if ((lane & (kSpread - 1)) == 0) sm.part[wave][lane / kSpread] = acc[0];
+    __syncthreads();
+    if (threadIdx.x < NV) {
+        const int q = threadIdx.x;
+        const float v = ((sm.part[0][q] + sm.part[1][q]) + sm.part[2][q]) + sm.part[3][q];
+        const int m = q / J;
+        if (m < nrows) {
+            const size_t idx = (size_t)(row0 + m) * R + j0 + q % J;
+            if constexpr (kFlagged) {
+                for (int c = 0; c < copies; ++c) store_v_flagged(V, idx + (size_t)c * copy_stride, v);
+            } else
+                V[idx] = v;
+        }
+    }
+    __syncthreads();  // sm is rewritten by the next block
+}
+
+template <typename T, int R, bool kFlagged, typename RM>
+__device__ __forceinline__ void shrink_segment_split(float *V, const T *X, const T *Ak, int d_in, int lo, int hi,
+                                                     int j0, RM rm, int copies, size_t copy_stride,
+                                                     ShrinkSplitSmem &sm) {
+    for (int row0 = lo; row0 < hi; row0 += 4) {
+        const int nrows = min(4, hi - row0);
+        shrink_block_split<T, R, 4, kFlagged>(V, X, Ak, d_in, row0, min(nrows, 4), j0, rm, copies, copy_stride, sm);
+    }
+}
+
 // All rows of one segment, rank row j, one wave. `arow_fn()` returns the
 // address of row j of the segment's A_k; rm(p) the row of X behind segment
 // row p.
@@ -252,7 +355,9 @@ __device__ __forceinline__ bool vector_segment(int lo, int hi, int k, int num_ad
     return (lo < hi) & (k >= 0) & (k < num_adapters) & !takes_mfma<T>(hi - lo);
 }
 
-// One vector-path shrink item: rank row j of segment s, one wave. Returns
+// One vector-path shrink item: rank row j of segment s, one wave (a segment
+// of kSplitRows rows or more: rank rows j0 .. j0 + 3, the workgroup, so
+// every wave of the workgroup must call this with the same segment). Returns
 // false if the segment is empty, names no valid adapter or belongs to the
 // MFMA path (then nothing is written).
 // Offsets that decrease at this segment (so that other segments may overlap)
@@ -265,7 +370,7 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
                                                    int num_adapters, const int32_t *seg_start,
                                                    const int32_t *seg_adapter, int s, int j, int M,
                                                    int d_in, int lane, RM rm, const WaitCtl &wc,
-                                                   int copies = 1) {
+                                                   ShrinkSplitSmem &split_sm, int copies = 1) {
     AdapterTable<kSpec> tab;
     tab.load(A_ptrs, num_adapters, lane);
     int lo, hi;
@@ -274,6 +379,12 @@ __device__ __forceinline__ bool shrink_vector_item(float *V, const T *X, const u
     const bool inverted = segment_rows(seg_start, s, M, lo, hi);
     if (inverted && j == 0 && lane == 0) report(wc, kStatusBadOffsets);
     if (!vector_segment<T>(lo, hi, k, num_adapters) | (st != 0)) return false;
+    if (hi - lo >= kSplitRows) {  // uniform across the workgroup
+        const T *Ak = reinterpret_cast<const T *>(tab.address(A_ptrs, k));
+        shrink_segment_split<T, R, kFlagged>(V, X, Ak, d_in, lo, hi, j - (int)threadIdx.x / kWave, rm, copies,
+                                             (size_t)M * R, split_sm);
+        return true;
+    }
     auto arow = [&]() { return reinterpret_cast<const T *>(tab.address(A_ptrs, k)) + (size_t)j * d_in; };
     shrink_segment_wave<T, R, kFlagged>(V, X, arow, d_in, lo, hi, j, lane, rm, copies, (size_t)M * R);
     return true;
@@ -598,12 +709,12 @@ struct MfmaAdapters {
 // Items [0, round_up_xcds(N) * R / 4): vector path, one per (segment, group of 4 rank rows),
 // skipping segments the MFMA path owns. Items after that: MFMA shrink items,
 // one per (16-row tile, part of d_in) (bf16 only).
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 __global__ __launch_bounds__(kBlock) void shrink_kernel(
     float *__restrict__ V, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     int num_adapters, const int32_t *__restrict__ seg_start,
     const int32_t *__restrict__ seg_adapter, int num_segments, int M, int d_in, int num_units, int ks,
-    int small, uint32_t *counters, float *partials, RowMap<kGather> rm, WaitCtl wc) {
+    uint32_t *counters, float *partials, RowMap<kGather> rm, WaitCtl wc) {
     constexpr int groups = R / kWavesPerBlock;
     const int gemv_items = round_up_xcds(num_segments) * groups;
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
@@ -612,19 +723,18 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         if (!vector_shrink_item(blockIdx.x, num_segments, groups, s, grp)) return;
         const int j = grp * kWavesPerBlock + (int)threadIdx.x / kWave;
         const int lane = threadIdx.x & (kWave - 1);
+        __shared__ ShrinkSplitSmem split_sm;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, false, true>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, lane, rm, wc);
+                                                  s, j, M, d_in, lane, rm, wc, split_sm);
         else
             shrink_vector_item<T, R, false, false>(V, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                   s, j, M, d_in, lane, rm, wc);
+                                                   s, j, M, d_in, lane, rm, wc, split_sm);
         return;
     }
     if constexpr (Elem<T>::kMfma) {
-        __shared__ union {
-            ShrinkSmem<R> s16;
-            Shrink64Smem<R> s64;
-        } sm;
+        // one tile kind per kernel: the other's registers and LDS are not paid for
+        __shared__ typename std::conditional<kSmall, ShrinkSmem<R>, Shrink64Smem<R>>::type sm;
         __shared__ PieceList pl;
         __shared__ int s_flag;
         int u, kp;
@@ -633,7 +743,7 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
         const MfmaAdapters ak_of(A_ptrs, num_adapters);
         const bf16_t *Xb = reinterpret_cast<const bf16_t *>(X);
         uint32_t *const split = ks > 1 ? counters + (size_t)u * kCounterStride : nullptr;
-        if (small) {
+        if constexpr (kSmall) {
             constexpr int CG = ShrinkSmem<R>::kGroups;
             const int cg = u % CG, pi = (u / CG) % kShrinkPieces, t = u / (CG * kShrinkPieces);
             const int t0 = t * kShrinkRows;
@@ -641,13 +751,13 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
                                  min(t0 + kShrinkRows, M));
             if (pi >= pl.n || st != 0) return;
             shrink_mfma_item<R, false, true>(V, Xb, ak_of, pl.p[pi], d_in, t, cg, u, kp, ks, split, partials,
-                                             sm.s16, &s_flag, rm, wc);
+                                             sm, &s_flag, rm, wc);
         } else {
             const int t0 = u * kShrinkTileRows;
             gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M, t0,
                                  min(t0 + kShrinkTileRows, M));
             if (pl.n == 0 || st != 0) return;
-            shrink_mfma_item64<R, false, true>(V, Xb, ak_of, pl, d_in, u, kp, ks, split, partials, sm.s64, &s_flag,
+            shrink_mfma_item64<R, false, true>(V, Xb, ak_of, pl, d_in, u, kp, ks, split, partials, sm, &s_flag,
                                                rm, wc);
         }
     }
@@ -656,11 +766,11 @@ __global__ __launch_bounds__(kBlock) void shrink_kernel(
 // ----------------------------------------------------------------------------
 // Expand: up to RB rows of one segment, VEC columns per lane.
 // ----------------------------------------------------------------------------
-template <typename T, int R, int RB, bool kFlagged, typename BkFn, typename Ready, typename Commit,
+template <typename T, int R, int RB, bool kFlagged, bool kBPre, typename BkFn, typename Ready, typename Commit,
           typename RM>
 __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, int d_out, int row0,
                                             int nrows, int n0, bool active, float scale, Ready ready,
-                                            Commit commit, RM rm, const WaitCtl &wc) {
+                                            Commit commit, RM rm, const WaitCtl &wc, const uint4 *bpre) {
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int JC = R < 16 ? R : 16;  // rank rows of B held in registers at a time
     // Loads are unconditional (see shrink_wave): an inactive lane reads
@@ -680,12 +790,13 @@ __device__ __forceinline__ void expand_rows(T *Y, const float *V, BkFn bk_fn, in
         for (int e = 0; e < VEC; ++e) acc[m][e] = 0.f;
     }
 
-    const T *Bk = bk_fn();  // after the Y loads: their address is known first
+    const T *Bk = kBPre ? nullptr : bk_fn();  // after the Y loads: their address is known first
 #pragma unroll 1
     for (int jc = 0; jc < R; jc += JC) {
         uint4 b[JC];
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj) b[jj] = ld16_stream(Bk + (size_t)(jc + jj) * d_out + nc);
+        for (int jj = 0; jj < JC; ++jj)
+            b[jj] = kBPre ? bpre[jc + jj] : ld16_stream(Bk + (size_t)(jc + jj) * d_out + nc);
         if (!ready()) return;  // uniform: V may be read from here on
         float vl = 0.f;  // flagged V: this lane's value of the block
         if constexpr (kFlagged) {
@@ -746,20 +857,30 @@ __device__ __forceinline__ void expand_segment(T *Y, const float *V, BkFn bk_fn,
                                                int hi, int n0, bool active, float scale, Ready ready,
                                                Commit commit, RM rm, const WaitCtl &wc) {
     static_assert(kMaxRB == 4 || kMaxRB == 8, "row blocks of 4 or 8");
+    // With R <= 16 the whole column slice of B_k fits in registers: it is
+    // requested once for the segment, and every row block reuses it.
+    constexpr bool kBPre = R <= 16;
+    uint4 bpre[kBPre ? R : 1];
+    if constexpr (kBPre) {
+        const T *Bk = bk_fn();
+        const int nc = active ? n0 : 0;
+#pragma unroll
+        for (int jj = 0; jj < R; ++jj) bpre[jj] = ld16_stream(Bk + (size_t)jj * d_out + nc);
+    }
     for (int row0 = lo; row0 < hi; row0 += kMaxRB) {
         const int nrows = min(kMaxRB, hi - row0);
         if (nrows == 1)
-            expand_rows<T, R, 1, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
-                                           rm, wc);
+            expand_rows<T, R, 1, kFlagged, kBPre>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready,
+                                                  commit, rm, wc, bpre);
         else if (nrows <= 2)
-            expand_rows<T, R, 2, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
-                                           rm, wc);
+            expand_rows<T, R, 2, kFlagged, kBPre>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready,
+                                                  commit, rm, wc, bpre);
         else if (kMaxRB == 4 || nrows <= 4)
-            expand_rows<T, R, 4, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
-                                           rm, wc);
+            expand_rows<T, R, 4, kFlagged, kBPre>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready,
+                                                  commit, rm, wc, bpre);
         else if constexpr (kMaxRB == 8)
-            expand_rows<T, R, 8, kFlagged>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready, commit,
-                                           rm, wc);
+            expand_rows<T, R, 8, kFlagged, kBPre>(Y, V, bk_fn, d_out, row0, nrows, n0, active, scale, ready,
+                                                  commit, rm, wc, bpre);
     }
 }
 
@@ -867,13 +988,13 @@ constexpr int kFusedRB = 4;
 // item layout (the workgroup id for a launch of one projection, the offset
 // inside the projection's region for a layer-batched launch; congruent to
 // the workgroup id modulo 8 either way, so the XCD placement is the same).
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 __device__ __forceinline__ void fused_item(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int num_units, int ks, int small, float scale, int long_batch, uint32_t *tile_counters,
+    int num_units, int ks, float scale, int long_batch, uint32_t *tile_counters,
     uint32_t *split_counters, float *Vws, float *Vpairs, float *partials, RowMap<kGather> rm, const WaitCtl &wc,
     const int item) {
     // The vector path hands V over as flagged pairs (Vpairs), one copy per
@@ -900,12 +1021,13 @@ __device__ __forceinline__ void fused_item(
         int s, grp;
         if (!vector_shrink_item(item, num_segments, groups, s, grp)) return;
         const int j = grp * kWavesPerBlock + tid / kWave;
+        __shared__ ShrinkSplitSmem split_sm;
         if (num_adapters <= kSpecTable)
             shrink_vector_item<T, R, true, true>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                 s, j, M, d_in, tid & (kWave - 1), rm, wc, ntiles_g);
+                                                 s, j, M, d_in, tid & (kWave - 1), rm, wc, split_sm, ntiles_g);
         else
             shrink_vector_item<T, R, true, false>(Vpairs, X, A_ptrs, num_adapters, seg_start, seg_adapter,
-                                                  s, j, M, d_in, tid & (kWave - 1), rm, wc, ntiles_g);
+                                                  s, j, M, d_in, tid & (kWave - 1), rm, wc, split_sm, ntiles_g);
         return;
     }
     if (item >= a1 && item < a2) {
@@ -934,9 +1056,9 @@ __device__ __forceinline__ void fused_item(
         return;
     }
     if constexpr (Elem<T>::kMfma) {
+        // one shrink tile kind per kernel: the other's registers and LDS are not paid for
         __shared__ union {
-            ShrinkSmem<R> s16;
-            Shrink64Smem<R> s64;
+            typename std::conditional<kSmall, ShrinkSmem<R>, Shrink64Smem<R>>::type shrink;
             ExpandSmem<R> expand;
         } sm;
         __shared__ PieceList pl;
@@ -951,7 +1073,7 @@ __device__ __forceinline__ void fused_item(
             uint32_t *const split = ks > 1 ? split_counters + (size_t)u * kCounterStride : nullptr;
             int done;
             int t64;
-            if (small) {
+            if constexpr (kSmall) {
                 constexpr int CG = ShrinkSmem<R>::kGroups;
                 const int cg = u % CG, pi = (u / CG) % kShrinkPieces, t = u / (CG * kShrinkPieces);
                 const int t0 = t * kShrinkRows;
@@ -959,7 +1081,7 @@ __device__ __forceinline__ void fused_item(
                                      t0, min(t0 + kShrinkRows, M));
                 if (pi >= pl.n || st != 0) return;
                 done = shrink_mfma_item<R, true, false>(Vws, Xb, ak_of, pl.p[pi], d_in, t, cg, u, kp, ks, split,
-                                                        partials, sm.s16, &s_flag, rm, wc);
+                                                        partials, sm.shrink, &s_flag, rm, wc);
                 t64 = t0 / kTileRows;
             } else {
                 const int t0 = u * kShrinkTileRows;
@@ -967,7 +1089,7 @@ __device__ __forceinline__ void fused_item(
                                      t0, min(t0 + kShrinkTileRows, M));
                 if (pl.n == 0 || st != 0) return;
                 done = shrink_mfma_item64<R, true, false>(Vws, Xb, ak_of, pl, d_in, u, kp, ks, split, partials,
-                                                          sm.s64, &s_flag, rm, wc);
+                                                          sm.shrink, &s_flag, rm, wc);
                 t64 = u;
             }
             if (done) publish(&tile_arrive[t64 * kCounterStride]);
@@ -989,7 +1111,7 @@ __device__ __forceinline__ void fused_item(
         auto ready = [&]() {
             if (state < 0) {
                 int units = 1;  // 64-row tiles: the tile itself
-                if (small) {
+                if constexpr (kSmall) {
                     units = 0;
                     for (int a = t0; a < t1; a += kShrinkRows) {
                         const int b = min(a + kShrinkRows, t1);
@@ -1030,7 +1152,7 @@ __device__ __forceinline__ void fused_item(
             reset_pair(&tile_arrive[t * kCounterStride], &tile_depart[t * kCounterStride]);
             // the split counters of its shrink tiles too: their parts all
             // passed their wait before publishing
-            const int units_per_tile = small ? ShrinkSmem<R>::kGroups * kShrinkPieces * kTileRows / kShrinkRows : 1;
+            const int units_per_tile = kSmall ? ShrinkSmem<R>::kGroups * kShrinkPieces * kTileRows / kShrinkRows : 1;
             if (ks > 1 && tid < units_per_tile) {
                 const int u = units_per_tile * t + tid;
                 if (u < num_units)
@@ -1041,16 +1163,16 @@ __device__ __forceinline__ void fused_item(
     }
 }
 
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 __global__ __launch_bounds__(kBlock) void fused_kernel(
     T *__restrict__ Y, const T *__restrict__ X, const uint64_t *__restrict__ A_ptrs,
     const uint64_t *__restrict__ B_ptrs, int num_adapters,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, int d_in, int d_out, int ntiles_g, int ntiles_m, int num_tiles,
-    int num_units, int ks, int small, float scale, int long_batch, uint32_t *tile_counters,
+    int num_units, int ks, float scale, int long_batch, uint32_t *tile_counters,
     uint32_t *split_counters, float *Vws, float *Vpairs, float *partials, RowMap<kGather> rm, WaitCtl wc) {
-    fused_item<T, R, kGather>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
-                              d_in, d_out, ntiles_g, ntiles_m, num_tiles, num_units, ks, small, scale, long_batch,
+    fused_item<T, R, kGather, kSmall>(Y, X, A_ptrs, B_ptrs, num_adapters, seg_start, seg_adapter, num_segments, M,
+                              d_in, d_out, ntiles_g, ntiles_m, num_tiles, num_units, ks, scale, long_batch,
                               tile_counters, split_counters, Vws, Vpairs, partials, rm, wc, (int)blockIdx.x);
 }
 
@@ -1062,7 +1184,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(
 // projection order. Inside a region every wait is on lower ids of the same
 // region (or on the sibling parts of a split shrink tile), so the argument
 // that a fused launch's waits end carries over unchanged.
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
     LayerArgs L, const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_adapter,
     int num_segments, int M, float scale, int long_batch, RowMap<kGather> rm) {
@@ -1107,15 +1229,14 @@ __global__ __launch_bounds__(kBlock) void fused_layer_kernel(
         d.num_tiles = ui(src.num_tiles);
         d.num_units = ui(src.num_units);
         d.ks = ui(src.ks);
-        d.small = ui(src.small);
         d.base = ui(src.base);
         d.items = ui(src.items);
     }
     const int item = b - d.base;
     if (item >= d.items) return;  // padding up to the next region
-    fused_item<T, R, kGather>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
+    fused_item<T, R, kGather, kSmall>(reinterpret_cast<T *>(d.Y), reinterpret_cast<const T *>(d.X), d.A_ptrs,
                               d.B_ptrs, d.num_adapters, seg_start, seg_adapter, num_segments, M, d.d_in,
-                              d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.num_units, d.ks, d.small, scale,
+                              d.d_out, d.ntiles_g, d.ntiles_m, d.num_tiles, d.num_units, d.ks, scale,
                               long_batch,
                               d.tile_counters, d.split_counters, d.Vws, d.Vpairs, d.partials, rm, L.wc, item);
 }
@@ -1137,7 +1258,7 @@ static int gemv_col_tiles(int d_out) {
     return (d_out + cols - 1) / cols;
 }
 
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     const ShrinkLayout L = shrink_layout(a.M, a.d_in, a.r, a.dtype);
     const int units = Elem<T>::kMfma ? L.plan.units : 0;
@@ -1145,9 +1266,9 @@ static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
                           (unsigned)(units ? mfma_shrink_items(units, ks) : 0);
     char *ws = static_cast<char *>(a.workspace);
-    hipLaunchKernelGGL((shrink_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st, a.V,
+    hipLaunchKernelGGL((shrink_kernel<T, R, kGather, kSmall>), dim3(grid), dim3(kBlock), 0, st, a.V,
                        reinterpret_cast<const T *>(a.X), a.A_ptrs, a.num_adapters, a.seg_start,
-                       a.seg_adapter, a.num_segments, a.M, a.d_in, units, ks, L.plan.small,
+                       a.seg_adapter, a.num_segments, a.M, a.d_in, units, ks,
                        ks > 1 ? reinterpret_cast<uint32_t *>(ws + L.counters) : nullptr,
                        ks > 1 ? reinterpret_cast<float *>(ws + L.partials) : nullptr,
                        RowMap<kGather>{a.rows, a.M},
@@ -1155,9 +1276,16 @@ static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Kernels are built per shrink tile kind (a bf16 batch of up to
+// kSmallBatchRows rows takes 16-row tiles, a larger one 64-row tiles);
+// batches without the MFMA path take the 16-row build.
 template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
-    return a.rows ? launch_shrink_g<T, R, true>(a, st) : launch_shrink_g<T, R, false>(a, st);
+    if constexpr (Elem<T>::kMfma) {
+        if (!small_tiles(a.M))
+            return a.rows ? launch_shrink_g<T, R, true, false>(a, st) : launch_shrink_g<T, R, false, false>(a, st);
+    }
+    return a.rows ? launch_shrink_g<T, R, true, true>(a, st) : launch_shrink_g<T, R, false, true>(a, st);
 }
 
 template <typename T, int R, bool kGather>
@@ -1187,7 +1315,7 @@ static hipError_t launch_expand_t(const ExpandArgs &a, hipStream_t st) {
     return a.rows ? launch_expand_g<T, R, true>(a, st) : launch_expand_g<T, R, false>(a, st);
 }
 
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
     const FusedLayout L = fused_layout(a.M, a.d_in, a.d_out, a.r, a.dtype);
     const int tiles = Elem<T>::kMfma ? L.tiles : 0;
@@ -1200,10 +1328,10 @@ static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
                           (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *tile_c = reinterpret_cast<uint32_t *>(ws + L.tile_counters);
-    hipLaunchKernelGGL((fused_kernel<T, R, kGather>), dim3(grid), dim3(kBlock), 0, st,
+    hipLaunchKernelGGL((fused_kernel<T, R, kGather, kSmall>), dim3(grid), dim3(kBlock), 0, st,
                        reinterpret_cast<T *>(a.Y), reinterpret_cast<const T *>(a.X), a.A_ptrs,
                        a.B_ptrs, a.num_adapters, a.seg_start, a.seg_adapter, a.num_segments, a.M,
-                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, units, L.plan.ks, L.plan.small, a.scale,
+                       a.d_in, a.d_out, ntiles_g, ntiles_m, tiles, units, L.plan.ks, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), tile_c,
                        reinterpret_cast<uint32_t *>(ws + L.split_counters),
                        reinterpret_cast<float *>(ws + L.v), reinterpret_cast<float *>(ws + L.vpairs),
@@ -1214,10 +1342,14 @@ static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
 
 template <typename T, int R>
 static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
-    return a.rows ? launch_fused_g<T, R, true>(a, st) : launch_fused_g<T, R, false>(a, st);
+    if constexpr (Elem<T>::kMfma) {
+        if (!small_tiles(a.M))
+            return a.rows ? launch_fused_g<T, R, true, false>(a, st) : launch_fused_g<T, R, false, false>(a, st);
+    }
+    return a.rows ? launch_fused_g<T, R, true, true>(a, st) : launch_fused_g<T, R, false, true>(a, st);
 }
 
-template <typename T, int R, bool kGather>
+template <typename T, int R, bool kGather, bool kSmall>
 static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
     LayerArgs L{};
     L.num_projections = a.num_projections;
@@ -1244,7 +1376,6 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         d.num_tiles = tiles;
         d.num_units = units;
         d.ks = FL.plan.ks;
-        d.small = FL.plan.small;
         char *w = ws + ws_off;
         d.tile_counters = reinterpret_cast<uint32_t *>(w + FL.tile_counters);
         d.split_counters = reinterpret_cast<uint32_t *>(w + FL.split_counters);
@@ -1258,7 +1389,7 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         base += round_up_xcds(d.items);
         ws_off += align256(FL.total);
     }
-    hipLaunchKernelGGL((fused_layer_kernel<T, R, kGather>), dim3((unsigned)base), dim3(kBlock), 0, st, L,
+    hipLaunchKernelGGL((fused_layer_kernel<T, R, kGather, kSmall>), dim3((unsigned)base), dim3(kBlock), 0, st, L,
                        a.seg_start, a.seg_adapter, a.num_segments, a.M, a.scale,
                        (int)((int64_t)a.M >= 16 * (int64_t)a.num_segments), RowMap<kGather>{a.rows, a.M});
     return hipGetLastError();
@@ -1266,7 +1397,12 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
 
 template <typename T, int R>
 static hipError_t launch_fused_layer_t(const LayerCall &a, hipStream_t st) {
-    return a.rows ? launch_fused_layer_g<T, R, true>(a, st) : launch_fused_layer_g<T, R, false>(a, st);
+    if constexpr (Elem<T>::kMfma) {
+        if (!small_tiles(a.M))
+            return a.rows ? launch_fused_layer_g<T, R, true, false>(a, st)
+                          : launch_fused_layer_g<T, R, false, false>(a, st);
+    }
+    return a.rows ? launch_fused_layer_g<T, R, true, true>(a, st) : launch_fused_layer_g<T, R, false, true>(a, st);
 }
 
 // Whether a bf16 batch can hold a segment long enough for the MFMA path:

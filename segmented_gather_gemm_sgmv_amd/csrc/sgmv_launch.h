@@ -69,7 +69,7 @@ struct LayerProj {
     uint32_t *tile_counters, *split_counters;
     float *Vws, *Vpairs, *partials;
     int num_adapters, d_in, d_out;
-    int ntiles_g, ntiles_m, num_tiles, num_units, ks, small;
+    int ntiles_g, ntiles_m, num_tiles, num_units, ks;
     int base;   // first workgroup id of the projection's region (a multiple of 8)
     int items;  // items of its own fused launch
 };

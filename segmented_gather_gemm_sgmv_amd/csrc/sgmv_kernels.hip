@@ -1012,9 +1012,15 @@ __device__ __forceinline__ void fused_item(
     constexpr int groups = R / kWavesPerBlock;
     __shared__ int s_flag;
     const int tid = threadIdx.x;
-    const int a0 = round_up_xcds(num_segments) * groups;  // vector shrink items
+    // Item regions, in dispatch order: producers first (vector shrink, MFMA
+    // shrink), then consumers (MFMA expand, vector expand). The MFMA expand
+    // tiles come before the vector expand items: they have more to do once
+    // V is there, and the vector items, which mostly wait for their
+    // segment's shrink, can take the last slots.
+    const int a0 = round_up_xcds(num_segments) * groups;   // vector shrink items
     const int a1 = a0 + mfma_shrink_items(num_units, ks);  // MFMA shrink items (unit x part)
-    const int a2 = a1 + num_segments * ntiles_g;     // vector expand items; MFMA expand after
+    const int aM = a1 + round_up_xcds(num_tiles * ntiles_m);  // MFMA expand tiles
+    const int a2 = aM + num_segments * ntiles_g;            // vector expand items
 
     if (num_adapters <= 0) return;  // no segment can name a valid adapter
     if (item < a0) {
@@ -1030,8 +1036,8 @@ __device__ __forceinline__ void fused_item(
                                                   s, j, M, d_in, tid & (kWave - 1), rm, wc, split_sm, ntiles_g);
         return;
     }
-    if (item >= a1 && item < a2) {
-        const int e = item - a1;
+    if (item >= aM && item < a2) {
+        const int e = item - aM;
         const int s = e / ntiles_g;
         const int tile = e % ntiles_g;
         const int n0 = (tile * kBlock + tid) * VEC;
@@ -1095,7 +1101,8 @@ __device__ __forceinline__ void fused_item(
             if (done) publish(&tile_arrive[t64 * kCounterStride]);
             return;
         }
-        const int e = xcd_local_item(item, a2, ((M + kTileRows - 1) / kTileRows) * ntiles_m);
+        if (item < a1 || item >= aM) return;
+        const int e = xcd_local_item(item, a1, num_tiles * ntiles_m);
         if (e < 0) return;
         const int t = e / ntiles_m;
         const int t0 = t * kTileRows;

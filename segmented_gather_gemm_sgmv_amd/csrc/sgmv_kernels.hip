@@ -581,15 +581,21 @@ __device__ int shrink_mfma_item64(float *V, const bf16_t *X, AkOf ak_of,
     f32x4_t res[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) res[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // pieces two at a time: one pass over this part of d_in per pair
-    for (int q = 0; q < pl.n; q += kPassPieces) {
+    // pieces kPassPieces at a time: one pass over this part of d_in each
+    constexpr int PP = Shrink64Smem<R>::kPassPieces;
+    for (int q = 0; q < pl.n; q += PP) {
         const Piece p0 = pl.p[q];
-        if (q + 1 < pl.n) {
-            const Piece p1 = pl.p[q + 1];
-            const bf16_t *const ak[2] = {ak_of(p0.k), ak_of(p1.k)};
-            const int lo[2] = {p0.lo, p1.lo}, hi[2] = {p0.hi, p1.hi};
-            shrink_tile64_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
-        } else {
+        bool two = false;
+        if constexpr (PP == 2) {
+            if (q + 1 < pl.n) {
+                const Piece p1 = pl.p[q + 1];
+                const bf16_t *const ak[2] = {ak_of(p0.k), ak_of(p1.k)};
+                const int lo[2] = {p0.lo, p1.lo}, hi[2] = {p0.hi, p1.hi};
+                shrink_tile64_mfma<R, 2>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);
+                two = true;
+            }
+        }
+        if (!two) {
             const bf16_t *const ak[1] = {ak_of(p0.k)};
             const int lo[1] = {p0.lo}, hi[1] = {p0.hi};
             shrink_tile64_mfma<R, 1>(X, ak, d_in, t0, lo, hi, ms0, ms1, sm, res, rm);

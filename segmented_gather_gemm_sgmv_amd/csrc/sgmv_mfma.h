@@ -433,21 +433,24 @@ __device__ __forceinline__ void shrink_tile_mfma(const bf16_t *X, const bf16_t *
 constexpr int kShrinkTileRows = 64;   // rows of a 64-row shrink tile (batches of many tiles)
 constexpr int kMacroK = 128;
 constexpr int kChunksPerRow = kMacroK * 2 / 16;   // 16-byte chunks per A_k row of a macro step
-constexpr int kPassPieces = 2;                    // pieces one pass over d_in can take
-
 template <int R>
 struct Shrink64Smem {
     static constexpr int kNB = R < 16 ? 1 : R / 16;                   // 16-column MFMA blocks
     static constexpr int kALoads = R * kChunksPerRow < kBlockThreads ? 1 : R * kChunksPerRow / kBlockThreads;
     static constexpr int kStages = R >= 64 ? 2 : (R >= 32 ? 3 : 4);   // macro steps in flight
+    // Pieces one pass over d_in can take. At r = 64 a pass takes one: two
+    // pieces' A_k chunks would need 64 KB of LDS, leaving room for one
+    // workgroup per CU; a tile that meets two segments then reads X twice.
+    static constexpr int kPassPieces = R >= 64 ? 1 : 2;
     uint4 a[2][kPassPieces][R * kChunksPerRow];
+    uint4 xs[kBlockThreads / 64][16 * kChunksPerRow];  // each wave's X rows of a step, staged
 };
 
 template <int R, int NP>
 struct Shrink64Stage {
     uint4 a[NP][Shrink64Smem<R>::kALoads];  // this thread's A_k chunks, per piece
-    uint4 x[4];                           // this lane's X elements, slices 0..3
-    uint32_t ok;                          // bits 0..3: X slice inside d_in; bits 4..: A chunk inside d_in
+    uint4 x[4];                           // this lane's X chunks: rows 4 q + lane / 16, chunk lane % 16
+    uint32_t ok;                          // bits 0..3: X chunk inside d_in; bits 4..: A chunk inside d_in
 };
 
 // Pieces lo[p] .. hi[p] - 1 (p < NP) are disjoint row ranges inside the tile,
@@ -477,8 +480,19 @@ __device__ void shrink_tile64_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP
         rhi = max(rhi, hi[p]);
         touches[p] = t0 + 16 * wave < hi[p] && t0 + 16 * wave + 16 > lo[p];
     }
-    // rows outside the pieces are never stored; rm gives the token row
-    const bf16_t *xrow = X + (size_t)rm(min(max(row, rlo), rhi - 1)) * d_in;
+    // X is loaded row-contiguously: in load q of a step, lane l takes chunk
+    // l % 16 (8 elements) of the wave's row 4 q + l / 16, so one instruction
+    // reads four whole 256-byte row segments (loads straight into the MFMA
+    // layout would touch 16 rows, 64 bytes each). The wave stages the step
+    // in its own LDS buffer, chunk c of row rho in slot c ^ rho, and reads it
+    // back in the MFMA layout. Rows outside the pieces are never stored; rm
+    // gives the token row.
+    (void)row;
+    const int xc = lane & 15;
+    const bf16_t *xrows[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        xrows[q] = X + (size_t)rm(min(max(t0 + 16 * wave + 4 * q + (lane >> 4), rlo), rhi - 1)) * d_in;
     // Every step of the loop is straight-line: a step past ms_end (padding to
     // a multiple of S) or a slice past d_in loads a clamped address and its
     // operands are zeroed, never skipped, so each group of loads stays in
@@ -492,10 +506,10 @@ __device__ void shrink_tile64_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP
         st.ok = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int k = kb + 32 * q + 8 * g;
+            const int k = kb + 8 * xc;
             const bool ok = step_ok && k < d_in;
             st.ok |= (uint32_t)ok << q;
-            st.x[q] = ld16_stream(xrow + (ok ? k : d_in - 8));
+            st.x[q] = ld16_stream(xrows[q] + (ok ? k : d_in - 8));
         }
 #pragma unroll
         for (int u = 0; u < kALoads; ++u) {
@@ -518,6 +532,13 @@ __device__ void shrink_tile64_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP
     // Consume one stage: its A_k chunks go to LDS buffer `buf`, then every
     // wave multiplies its X slices with the chunk of each piece it touches.
     auto consume = [&](const Shrink64Stage<R, NP> &st, int buf) {
+        // this wave's X rows first: LDS operations of a wave complete in
+        // order, so its reads below see them without a barrier
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rho = 4 * q + (lane >> 4);
+            sm.xs[wave][rho * kChunksPerRow + (xc ^ rho)] = ((st.ok >> q) & 1u) ? st.x[q] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < kALoads; ++u) {
             const int id = u * kBlockThreads + tid;
@@ -533,7 +554,7 @@ __device__ void shrink_tile64_mfma(const bf16_t *X, const bf16_t *const (&Ak)[NP
         lds_barrier();
         uint4 xq[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xq[q] = ((st.ok >> q) & 1u) ? st.x[q] : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) xq[q] = sm.xs[wave][i * kChunksPerRow + ((4 * q + g) ^ i)];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (NP > 1 && !touches[p]) continue;  // uniform

@@ -957,18 +957,18 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
         if (e < 0) return;
         const int t0 = (e / ntiles_m) * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
-        const int n0 = (e % ntiles_m) * kExpandTileCols;
+        const int n0 = (e % ntiles_m) * kExpandTileCols * expand_halves(false);
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
         auto load_v4 = [&](size_t idx) { return *reinterpret_cast<const float4 *>(V + idx); };
         auto ready = []() { return true; };
         if constexpr (kMaxRB == 4) {  // a batch of long segments: most tiles have pieces
             const SegPrefetch pre = prefetch_segments(seg_start, seg_adapter, num_segments);
-            expand_tile_mfma<R, true, true>(
+            expand_tile_mfma<R, expand_halves(false), true, true>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
                 [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
                 bk_of, load_v4, ready, rm);
         } else {
-            expand_tile_mfma<R, true, false>(
+            expand_tile_mfma<R, expand_halves(false), true, false>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm, pl,
                 [&]() {
                     gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
@@ -1113,7 +1113,7 @@ __device__ __forceinline__ void fused_item(
         const int t = e / ntiles_m;
         const int t0 = t * kTileRows;
         const int t1 = min(t0 + kTileRows, M);
-        const int n0 = (e % ntiles_m) * kExpandTileCols;
+        const int n0 = (e % ntiles_m) * kExpandTileCols * expand_halves(!kSmall);
         const uint32_t st = read_status(wc);
         const MfmaAdapters bk_of(B_ptrs, num_adapters);
         // V of these rows is complete once every part of every shrink unit
@@ -1146,12 +1146,12 @@ __device__ __forceinline__ void fused_item(
         };
         if (long_batch) {  // segments of 16 rows or more on average: most tiles have pieces
             const SegPrefetch pre = prefetch_segments(seg_start, seg_adapter, num_segments);
-            expand_tile_mfma<R, false, true>(
+            expand_tile_mfma<R, expand_halves(!kSmall), false, true>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
                 [&]() { gather_pieces<true>(pl, pre, seg_start, seg_adapter, num_segments, num_adapters, M, t0, t1); },
                 bk_of, load_v4, ready, rm);
         } else {
-            expand_tile_mfma<R, false, false>(
+            expand_tile_mfma<R, expand_halves(!kSmall), false, false>(
                 reinterpret_cast<bf16_t *>(Y), M, d_out, t0, n0, scale, sm.expand, pl,
                 [&]() {
                     gather_pieces<false>(pl, SegPrefetch{}, seg_start, seg_adapter, num_segments, num_adapters, M,
@@ -1305,7 +1305,7 @@ template <typename T, int R, bool kGather>
 static hipError_t launch_expand_g(const ExpandArgs &a, hipStream_t st) {
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
     const int tiles = Elem<T>::kMfma ? mfma_tiles(a.dtype, a.M) : 0;
-    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const int ntiles_m = tiles ? ceil_div(a.d_out, kExpandTileCols * expand_halves(false)) : 0;
     const unsigned grid = (unsigned)a.num_segments * ntiles_g + (unsigned)round_up_xcds(tiles * ntiles_m);
     // Batches of short segments (under 16 rows on average) run mostly on the
     // vector path: rows 8 at a time read B_k half as often. Batches of long
@@ -1334,7 +1334,7 @@ static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
     const int tiles = Elem<T>::kMfma ? L.tiles : 0;
     const int units = Elem<T>::kMfma ? L.plan.units : 0;
     const int ntiles_g = gemv_col_tiles<T>(a.d_out);
-    const int ntiles_m = tiles ? (a.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+    const int ntiles_m = tiles ? ceil_div(a.d_out, kExpandTileCols * expand_halves(!kSmall)) : 0;
     if (ntiles_g != L.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
     const unsigned grid = (unsigned)round_up_xcds(a.num_segments) * (R / kWavesPerBlock) +
                           (unsigned)(units ? mfma_shrink_items(units, L.plan.ks) : 0) +
@@ -1385,7 +1385,7 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
         const int units = Elem<T>::kMfma ? FL.plan.units : 0;
         d.ntiles_g = gemv_col_tiles<T>(in.d_out);
         if (d.ntiles_g != FL.copies) return hipErrorInvalidValue;  // one V copy per vector expand tile
-        d.ntiles_m = tiles ? (in.d_out + kExpandTileCols - 1) / kExpandTileCols : 0;
+        d.ntiles_m = tiles ? ceil_div(in.d_out, kExpandTileCols * expand_halves(!kSmall)) : 0;
         d.num_tiles = tiles;
         d.num_units = units;
         d.ks = FL.plan.ks;

@@ -36,7 +36,12 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kLongRows = 16;           // segments this long or longer take the MFMA path
 constexpr int kTileRows = 64;           // batch rows per MFMA tile (4 waves x 16)
-constexpr int kExpandTileCols = 128;    // d_out columns per expand tile
+constexpr int kExpandTileCols = 128;    // d_out columns per expand tile half
+// 128-column halves per MFMA expand workgroup: two in the fused launch of a
+// batch of many tiles (prefill), where fewer, longer workgroups wait once
+// for the loads of both halves; one elsewhere, where more workgroups in
+// flight matter more.
+__host__ __device__ constexpr int expand_halves(bool fused_many_tiles) { return fused_many_tiles ? 2 : 1; }
 constexpr int kMaxPieces = 8;           // long segments one window of a tile can meet
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -654,16 +659,19 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Expand tile: Y[m, n0:n0+128] += scale * V[m, :] . B_k[:, n0:n0+128] for
-// the rows m of every piece (segment with its adapter) of the 64-row tile
-// at t0. With kEarly the Y tile, and V when kVEarly, are requested before
-// the tile's pieces are known, so the segment metadata round trip overlaps
-// theirs (`gather()` collects the pieces into pl, from metadata the caller
-// requested before anything else). That pays when most tiles have pieces;
-// in a batch of short segments most tiles have none, and then the early
-// loads would be wasted, so without kEarly they wait for the pieces. Pieces
-// are taken one after another: each stages its B_k tile, updates its rows
-// of the Y tile held in registers, and the tile is stored once at the end.
+// Expand tile: Y[m, n0:n0+128 NT] += scale * V[m, :] . B_k[:, n0:n0+128 NT]
+// for the rows m of every piece (segment with its adapter) of the 64-row
+// tile at t0, taken as NT column halves of 128 that share the tile's V,
+// pieces and rows. With kEarly the Y tile, and V when kVEarly, are requested
+// before the tile's pieces are known, so the segment metadata round trip
+// overlaps theirs (`gather()` collects the pieces into pl, from metadata the
+// caller requested before anything else). That pays when most tiles have
+// pieces; in a batch of short segments most tiles have none, and then the
+// early loads would be wasted, so without kEarly they wait for the pieces.
+// Pieces are taken one after another: the B_k tiles of all NT halves are
+// requested together, then each half in turn is staged, multiplied and
+// added into its part of the Y tile held in registers; the tile is stored
+// once at the end. A workgroup thus waits once for the loads of NT halves.
 //
 // `ready()` is called by every thread once the first B tile is on its way
 // and before V is read (a consumer of V produced in the same launch waits
@@ -672,7 +680,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // requested together with Y.
 // load_v4(idx): V[idx .. idx + 3] (idx a multiple of 4).
 // rm(p, ok): the row of Y that segment row p updates (never stored if !ok).
-template <int R, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready,
+template <int R, int NT, bool kVEarly, bool kEarly, typename Gather, typename BkOf, typename LoadV4, typename Ready,
           typename RM>
 __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, int t0, int n0, float scale,
                                  ExpandSmem<R> &sm, const PieceList &pl, Gather gather, BkOf bk_of,
@@ -688,22 +696,29 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
     const int g = lane >> 4;
     const int i = lane & 15;
     const int t1 = min(t0 + kTileRows, M);
+    int nh = 0;  // halves inside d_out (uniform)
+#pragma unroll
+    for (int h = 0; h < NT; ++h) nh += n0 + h * kExpandTileCols < d_out;
 
-    // The Y tile: each thread owns kYPer vectors of 8. Rows past the batch
-    // and columns past d_out load a clamped address and are never stored.
+    // The Y tile: each thread owns kYPer vectors of 8 per half. Rows past the
+    // batch and columns past d_out load a clamped address and are never
+    // stored.
     constexpr int kYPer = kTileRows * kColVecs / kBlockThreads;
-    uint4 yv[kYPer];
-    int yrow[kYPer];    // row of Y behind each vector
+    uint4 yv[NT][kYPer];
+    int yrow[kYPer];    // row of Y behind each vector (the same in every half)
     uint32_t yok = 0;   // bit q: yrow[q] may be stored
     auto fetch_y = [&]() {
 #pragma unroll
         for (int q = 0; q < kYPer; ++q) {
             const int idx = tid + q * kBlockThreads;
-            const int n = n0 + (idx % kColVecs) * 8;
             bool ok;
             yrow[q] = rm(min(t0 + idx / kColVecs, t1 - 1), ok);
             yok |= (uint32_t)ok << q;
-            yv[q] = ld16(Y + (size_t)yrow[q] * d_out + (n < d_out ? n : 0));
+#pragma unroll
+            for (int h = 0; h < NT; ++h) {
+                const int n = n0 + h * kExpandTileCols + (idx % kColVecs) * 8;
+                yv[h][q] = ld16(Y + (size_t)yrow[q] * d_out + (n < d_out ? n : 0));
+            }
         }
     };
 
@@ -757,89 +772,113 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
         fetch_y();
         if constexpr (kVEarly) fetch_v();
     }
+    // B tile of one half: thread tid holds, for each of its (rank-row pair,
+    // column vector) items, the two rank rows' 16-byte vectors.
+    constexpr int kBItems = (R / 2) * kColVecs;
+    constexpr int kBPer = (kBItems + kBlockThreads - 1) / kBlockThreads;
     uint32_t touched = 0;  // bit q: Y vector q belongs to a piece
     for (int pi = 0; pi < pl.n; ++pi) {
         const Piece pc = pl.p[pi];
         const bf16_t *Bk = bk_of(pc.k);
-        // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
-        for (int idx = tid; idx < (R / 2) * kColVecs; idx += kBlockThreads) {
-            const int jp = idx / kColVecs;
-            const int c8 = idx % kColVecs;
-            const int n = n0 + c8 * 8 < d_out ? n0 + c8 * 8 : 0;  // columns past d_out are never stored
-            const uint4 r0 = ld16(Bk + (size_t)(2 * jp) * d_out + n);
-            const uint4 r1 = ld16(Bk + (size_t)(2 * jp + 1) * d_out + n);
-            const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-            const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+        uint4 bq[NT][kBPer][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo16 = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-                const uint32_t hi16 = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
-                *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
+        for (int h = 0; h < NT; ++h)
+#pragma unroll
+            for (int u = 0; u < kBPer; ++u) {
+                const int idx = min(tid + u * kBlockThreads, kBItems - 1);  // repeats are never staged
+                const int jp = idx / kColVecs;
+                const int n = n0 + h * kExpandTileCols + (idx % kColVecs) * 8;
+                const int nc = n < d_out ? n : 0;  // columns past d_out are never stored
+                bq[h][u][0] = ld16(Bk + (size_t)(2 * jp) * d_out + nc);
+                bq[h][u][1] = ld16(Bk + (size_t)(2 * jp + 1) * d_out + nc);
             }
-        }
-        if constexpr (R < K) {  // zero the padded part of the reduction
-            for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
-                sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
-        }
-        if (pi == 0) {
-            if (!ready()) return;  // uniform
-            if constexpr (!kVEarly) fetch_v();
-            split_v();
-        }
-        __syncthreads();  // B tile in LDS
-
-        // All B operands first, then eight independent accumulator chains, so
-        // neither LDS nor MFMA latency sits between consecutive instructions.
-        constexpr int NBLK = kExpandTileCols / 16;
-        uint4 bv[KS][NBLK];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int h = 0; h < NT; ++h) {
+            if (h >= nh) break;  // uniform
+            // B tile -> LDS, transposed: two rank rows per pass, packed as pairs.
+#pragma unroll
+            for (int u = 0; u < kBPer; ++u) {
+                const int idx = tid + u * kBlockThreads;
+                if (idx >= kBItems) continue;
+                const int jp = idx / kColVecs;
+                const int c8 = idx % kColVecs;
+                const uint4 r0 = bq[h][u][0], r1 = bq[h][u][1];
+                const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+                const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t lo16 = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
+                    const uint32_t hi16 = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
+                    *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
+                }
+            }
+            if constexpr (R < K) {  // zero the padded part of the reduction
+                for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
+                    sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
+            }
+            if (pi == 0 && h == 0) {
+                if (!ready()) return;  // uniform
+                if constexpr (!kVEarly) fetch_v();
+                split_v();
+            }
+            __syncthreads();  // B tile in LDS
+
+            // All B operands first, then eight independent accumulator chains, so
+            // neither LDS nor MFMA latency sits between consecutive instructions.
+            constexpr int NBLK = kExpandTileCols / 16;
+            uint4 bv[KS][NBLK];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int b = 0; b < NBLK; ++b)
+                    bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
+            f32x4_t acc[NBLK];
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(ahi[ks], as_bf16x8(bv[ks][b]), acc[b]);
+#pragma unroll
+                for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(alo[ks], as_bf16x8(bv[ks][b]), acc[b]);
+            }
+            __syncthreads();  // every wave is done with the B tile, whose LDS the delta tile reuses
 #pragma unroll
             for (int b = 0; b < NBLK; ++b)
-                bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
-        f32x4_t acc[NBLK];
 #pragma unroll
-        for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(ahi[ks], as_bf16x8(bv[ks][b]), acc[b]);
-#pragma unroll
-            for (int b = 0; b < NBLK; ++b) acc[b] = mfma_bf16(alo[ks], as_bf16x8(bv[ks][b]), acc[b]);
-        }
-        __syncthreads();  // every wave is done with the B tile, whose LDS the delta tile reuses
-#pragma unroll
-        for (int b = 0; b < NBLK; ++b)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[b][v];
-        __syncthreads();  // delta tile in LDS
+                for (int v = 0; v < 4; ++v) sm.ys[(16 * wave + 4 * g + v) * kYs + 16 * b + i] = acc[b][v];
+            __syncthreads();  // delta tile in LDS
 
+#pragma unroll
+            for (int q = 0; q < kYPer; ++q) {
+                const int idx = tid + q * kBlockThreads;
+                const int r = idx / kColVecs;
+                const int c8 = idx % kColVecs;
+                const int m = t0 + r;
+                if (m >= pc.lo && m < pc.hi) {
+                    const float4 d0 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8]);
+                    const float4 d1 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8 + 4]);
+                    const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                    float y[8];
+                    widen<bf16_t>(yv[h][q], y);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = y[e] + scale * d[e];
+                    yv[h][q] = narrow<bf16_t>(y);
+                    touched |= 1u << q;
+                }
+            }
+            __syncthreads();  // LDS free for the next half or piece
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < NT; ++h) {
 #pragma unroll
         for (int q = 0; q < kYPer; ++q) {
             const int idx = tid + q * kBlockThreads;
-            const int r = idx / kColVecs;
-            const int c8 = idx % kColVecs;
-            const int m = t0 + r;
-            if (m >= pc.lo && m < pc.hi) {
-                const float4 d0 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8]);
-                const float4 d1 = *reinterpret_cast<const float4 *>(&sm.ys[r * kYs + c8 * 8 + 4]);
-                const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                float y[8];
-                widen<bf16_t>(yv[q], y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = y[e] + scale * d[e];
-                yv[q] = narrow<bf16_t>(y);
-                touched |= 1u << q;
-            }
+            const int n = n0 + h * kExpandTileCols + (idx % kColVecs) * 8;
+            const int row = RM::kIndexed ? yrow[q] : t0 + idx / kColVecs;  // contiguous: a touched row is in the tile
+            if ((((touched & yok) >> q) & 1u) && n < d_out) st16(Y + (size_t)row * d_out + n, yv[h][q]);
         }
-        __syncthreads();  // LDS free for the next piece
-    }
-#pragma unroll
-    for (int q = 0; q < kYPer; ++q) {
-        const int idx = tid + q * kBlockThreads;
-        const int n = n0 + (idx % kColVecs) * 8;
-        const int row = RM::kIndexed ? yrow[q] : t0 + idx / kColVecs;  // contiguous: a touched row is in the tile
-        if ((((touched & yok) >> q) & 1u) && n < d_out) st16(Y + (size_t)row * d_out + n, yv[q]);
     }
 }
 

@@ -13,15 +13,19 @@
 // across the segment's rows held in registers, so decode segments (a handful
 // of rows) run at the rate weights stream in from HBM.
 //
-//  * shrink: one wave per (segment, rank row j). Row j of A_k (stored r x
-//    d_in, each row contiguous) is streamed in 16-byte loads, eight in flight
-//    per lane; each lane keeps a partial dot product per segment row, and one
-//    recursive-halving shuffle reduction per wave finishes them. No LDS, no
-//    barrier, no atomics: results are bitwise reproducible.
+//  * shrink: one workgroup per (segment, group of four rank rows). For a
+//    segment of one or two rows each wave takes one rank row j: row j of
+//    A_k (stored r x d_in, each row contiguous) is streamed in 16-byte
+//    loads, all in flight at once for d_in = 4096; each lane keeps a partial
+//    dot product per segment row, and one recursive-halving shuffle
+//    reduction per wave finishes them. For a longer segment the four waves
+//    split d_in instead, each covering the four rank rows for a block of
+//    rows, and their sums meet in LDS in wave order. No atomics: results are
+//    bitwise reproducible.
 //  * expand: one workgroup per (segment, tile of d_out columns). B_k (stored
-//    r x d_out) is streamed row by row, 16 bytes per lane; V of the segment's
-//    rows is uniform across the workgroup and comes in through scalar loads; Y
-//    is read, updated in fp32 and rounded once on store.
+//    r x d_out) is streamed row by row, 16 bytes per lane (once per segment
+//    for r <= 16); V of the segment's rows is uniform across the workgroup;
+//    Y is read, updated in fp32 and rounded once on store.
 //  * fused: one launch; workgroups with the lowest ids do the shrink work,
 //    the rest the expand work. An expand workgroup requests its B and Y,
 //    then waits for V from its segment's shrink workgroups, which have lower
@@ -981,7 +985,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 
 // ----------------------------------------------------------------------------
 // Fused: every shrink item (vector, then MFMA tiles) has a lower workgroup id
-// than every expand item (vector, then MFMA tiles).
+// than every expand item (MFMA tiles, then vector).
 // ----------------------------------------------------------------------------
 
 // Row blocks of 4 in the fused kernel's vector expand keep its register

@@ -14,17 +14,20 @@
 // consecutive elements of the reduction dimension as long as its A and B
 // operands agree on which ones.
 //
-//  * shrink tile: D = X_rows (64 x d_in) . A_k^T (d_in x r) on 64-row
-//    tiles, one wave per 16 rows; A_k is shared by the waves through LDS,
-//    X goes straight into registers, d_in may be split over several
-//    workgroups whose partial tiles are summed in a fixed order. fp32
-//    accumulation.
+//  * shrink tile: D = X_rows . A_k^T (d_in x r), fp32 accumulation, in one
+//    of two tile kinds (see "Two shrink tiles" below): 16-row tiles whose
+//    four waves split d_in (batches of up to 2048 rows), or 64-row tiles with
+//    one wave per 16 rows sharing A_k through LDS (larger batches). Both
+//    load X and A_k row-contiguously and reach the MFMA layout through LDS;
+//    d_in may be split over several workgroups whose partial tiles are
+//    summed in a fixed order.
 //  * expand piece: D = V_rows (16 x r) . B_k (r x 128 columns). V is fp32 and
 //    enters the A operand as two bf16 halves, hi = rne(v) and lo = rne(v - hi),
 //    so hi + lo carries 16 significant bits; both halves meet the same B
 //    operand. B_k is stored r x d_out (columns contiguous), so it is
 //    transposed through LDS on its way in; the result is staged through LDS
-//    so that Y is read and written in whole 16-byte vectors per lane.
+//    so that Y is read and written in whole 16-byte vectors per lane. A
+//    workgroup takes one or two 128-column halves of a 64-row tile.
 #pragma once
 
 #include "sgmv_common.h"

@@ -220,18 +220,17 @@ __device__ __forceinline__ void shrink_wave(float *V, const T *X, ArowFn arow_fn
 }
 
 // Segments of kSplitRows rows or more take the shrink a workgroup at a
-// time: the four waves split d_in, and each covers a block of up to 4 rows
-// and the workgroup's four rank rows j0 .. j0 + 3. A wave then streams its
-// quarter of the block's X rows and of the four A_k rows, so X crosses the
-// L1 once per workgroup instead of once per rank row, and a wave's loads
-// fit in flight at once (d_in = 4096: two 16-byte vectors per lane and
-// row). The partial sums meet in LDS and are added in wave order. (Blocks
-// of 8 rows would halve the passes but cost the fused kernel its
-// occupancy.)
+// time: the four waves split d_in, and each covers a block of up to 8 rows
+// (4 in some launches, see shrink_segment_split) and the workgroup's four
+// rank rows j0 .. j0 + 3. A wave then streams its quarter of the block's X
+// rows and of the four A_k rows, so X crosses the L1 once per workgroup
+// instead of once per rank row, and a wave's loads fit in flight at once
+// (d_in = 4096: two 16-byte vectors per lane and row). The partial sums
+// meet in LDS and are added in wave order.
 constexpr int kSplitRows = 3;
 
 struct ShrinkSplitSmem {
-    float part[kWavesPerBlock][4 * kWavesPerBlock];  // [wave][row * 4 + rank row]
+    float part[kWavesPerBlock][8 * kWavesPerBlock];  // [wave][row * 4 + rank row]
 };
 
 template <typename T, int R, int ROWS, bool kFlagged, typename RM>
@@ -242,7 +241,7 @@ __device__ __forceinline__ void shrink_block_split(float *V, const T *X, const T
     constexpr int J = kWavesPerBlock;
     constexpr int NV = ROWS * J;
     constexpr int U = 2;  // (ROWS + 4) * U vectors in flight per lane
-    static_assert(ROWS * J <= 4 * kWavesPerBlock, "one block's partial sums fit the LDS buffer");
+    static_assert(ROWS * J <= 8 * kWavesPerBlock, "one block's partial sums fit the LDS buffer");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nvec = d_in / VEC;
@@ -275,20 +274,24 @@ __device__ __forceinline__ void shrink_block_split(float *V, const T *X, const T
         for (int jj = 0; jj < J; ++jj)
 #pragma unroll
             for (int u = 0; u < U; ++u) a[jj][u] = ld16_stream(Ak + (size_t)(j0 + jj) * d_in + (size_t)vc[u] * VEC);
+        // the four A_k vectors of a column widened once, each X vector widened
+        // where it is used: few values live at a time
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            float af[J][VEC];
 #pragma unroll
             for (int jj = 0; jj < J; ++jj) {
                 if (!ok[u]) a[jj][u] = make_uint4(0, 0, 0, 0);
-                float af[VEC];
-                widen<T>(a[jj][u], af);
+                widen<T>(a[jj][u], af[jj]);
+            }
 #pragma unroll
-                for (int m = 0; m < ROWS; ++m) {
-                    float xf[VEC];
-                    widen<T>(x[m][u], xf);
+            for (int m = 0; m < ROWS; ++m) {
+                float xf[VEC];
+                widen<T>(x[m][u], xf);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[m * J + jj] = fmaf(xf[e], af[e], acc[m * J + jj]);
-                }
+                for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[m * J + jj] = fmaf(xf[e], af[jj][e], acc[m * J + jj]);
             }
         }
     }
@@ -315,9 +318,18 @@ template <typename T, int R, bool kFlagged, typename RM>
 __device__ __forceinline__ void shrink_segment_split(float *V, const T *X, const T *Ak, int d_in, int lo, int hi,
                                                      int j0, RM rm, int copies, size_t copy_stride,
                                                      ShrinkSplitSmem &sm) {
-    for (int row0 = lo; row0 < hi; row0 += 4) {
-        const int nrows = min(4, hi - row0);
-        shrink_block_split<T, R, 4, kFlagged>(V, X, Ak, d_in, row0, min(nrows, 4), j0, rm, copies, copy_stride, sm);
+    // Blocks of up to 8 rows take half the passes of blocks of 4. Launches
+    // for batches with no segment of 16 rows or more keep blocks of 4: they
+    // have little room for segments of several rows, and the registers of
+    // 8-row blocks would cost their other items (segments of one or two
+    // rows) a workgroup per CU at some ranks.
+    constexpr int kRows = std::is_same<T, bf16_short_t>::value ? 4 : 8;
+    for (int row0 = lo; row0 < hi; row0 += kRows) {
+        const int nrows = min(kRows, hi - row0);
+        if (nrows <= 4)
+            shrink_block_split<T, R, 4, kFlagged>(V, X, Ak, d_in, row0, nrows, j0, rm, copies, copy_stride, sm);
+        else
+            shrink_block_split<T, R, 8, kFlagged>(V, X, Ak, d_in, row0, nrows, j0, rm, copies, copy_stride, sm);
     }
 }
 

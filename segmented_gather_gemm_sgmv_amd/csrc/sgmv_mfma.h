@@ -779,11 +779,8 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
     // column vector) items, the two rank rows' 16-byte vectors.
     constexpr int kBItems = (R / 2) * kColVecs;
     constexpr int kBPer = (kBItems + kBlockThreads - 1) / kBlockThreads;
-    uint32_t touched = 0;  // bit q: Y vector q belongs to a piece
-    for (int pi = 0; pi < pl.n; ++pi) {
-        const Piece pc = pl.p[pi];
-        const bf16_t *Bk = bk_of(pc.k);
-        uint4 bq[NT][kBPer][2];
+    auto load_b = [&](uint4 (&bq)[NT][kBPer][2], int k) {
+        const bf16_t *Bk = bk_of(k);
 #pragma unroll
         for (int h = 0; h < NT; ++h)
 #pragma unroll
@@ -795,6 +792,24 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
                 bq[h][u][0] = ld16(Bk + (size_t)(2 * jp) * d_out + nc);
                 bq[h][u][1] = ld16(Bk + (size_t)(2 * jp + 1) * d_out + nc);
             }
+    };
+    // In a batch of short segments (no kEarly; the pieces are known here and
+    // a tile often meets several) the next piece's B tile is requested while
+    // this piece is worked on, so a tile waits once for B, not once per
+    // piece. The last piece asks for its own tile again (a cache hit): the
+    // request stays unconditional, which keeps the compiler from waiting for
+    // it where a branch around it would end.
+    constexpr bool kAhead = !kEarly && NT == 1;
+    uint32_t touched = 0;  // bit q: Y vector q belongs to a piece
+    uint4 bq[NT][kBPer][2];
+    if constexpr (kAhead) load_b(bq, pl.p[0].k);
+    for (int pi = 0; pi < pl.n; ++pi) {
+        const Piece pc = pl.p[pi];
+        uint4 bn[NT][kBPer][2];
+        if constexpr (kAhead)
+            load_b(bn, pl.p[min(pi + 1, pl.n - 1)].k);
+        else
+            load_b(bq, pc.k);
 #pragma unroll
         for (int h = 0; h < NT; ++h) {
             if (h >= nh) break;  // uniform
@@ -871,6 +886,15 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
                 }
             }
             __syncthreads();  // LDS free for the next half or piece
+        }
+        if constexpr (kAhead) {
+#pragma unroll
+            for (int h = 0; h < NT; ++h)
+#pragma unroll
+                for (int u = 0; u < kBPer; ++u) {
+                    bq[h][u][0] = bn[h][u][0];
+                    bq[h][u][1] = bn[h][u][1];
+                }
         }
     }
 #pragma unroll

@@ -656,6 +656,12 @@ struct ExpandSmem {
         float ys[kTileRows * kYsStride];                         // delta tile, [m][n]
     };
     static_assert(kBtStride % 8 == 0, "B tile rows must be whole 16-byte vectors");
+    // Position of the 16-byte chunk c (rank elements 8c .. 8c + 7) in row n:
+    // the chunks of a row are permuted by n / 8. A thread transposes eight
+    // consecutive columns (rows n = 8 c8 + e) at once, so without the
+    // permutation the 16 threads of a wave writing rows 8 c8 + e (same e)
+    // would all hit one LDS bank.
+    static __device__ __forceinline__ int chunk(int n, int c) { return c ^ ((n >> 3) & (kK / 8 - 1)); }
 };
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -827,12 +833,16 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t lo16 = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
                     const uint32_t hi16 = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
-                    *reinterpret_cast<uint32_t *>(&sm.bt[(c8 * 8 + e) * kBt + 2 * jp]) = lo16 | (hi16 << 16);
+                    const int n = c8 * 8 + e;
+                    *reinterpret_cast<uint32_t *>(&sm.bt[n * kBt + 8 * ExpandSmem<R>::chunk(n, jp >> 2) +
+                                                         2 * (jp & 3)]) = lo16 | (hi16 << 16);
                 }
             }
             if constexpr (R < K) {  // zero the padded part of the reduction
-                for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads)
-                    sm.bt[(idx / (K - R)) * kBt + R + idx % (K - R)] = 0;
+                for (int idx = tid; idx < kExpandTileCols * (K - R); idx += kBlockThreads) {
+                    const int n = idx / (K - R), k = R + idx % (K - R);
+                    sm.bt[n * kBt + 8 * ExpandSmem<R>::chunk(n, k >> 3) + (k & 7)] = 0;
+                }
             }
             if (pi == 0 && h == 0) {
                 if (!ready()) return;  // uniform
@@ -849,7 +859,7 @@ __device__ __forceinline__ void expand_tile_mfma(bf16_t *Y, int M, int d_out, in
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int b = 0; b < NBLK; ++b)
-                    bv[ks][b] = sm.bt16[((16 * b + i) * kBt + ks * 32 + 8 * g) / 8];
+                    bv[ks][b] = sm.bt16[((16 * b + i) * kBt + 8 * ExpandSmem<R>::chunk(16 * b + i, 4 * ks + g)) / 8];
             f32x4_t acc[NBLK];
 #pragma unroll
             for (int b = 0; b < NBLK; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};

@@ -71,15 +71,18 @@ inline int shrink_ksplit16(int M, int d_in, int r) {
 }
 
 // 64-row tiles: d_in is split over up to 8 workgroups per tile, enough for
-// about two workgroups per CU over the batch's tiles, with at least four
+// about `target` workgroups over the batch's tiles, with at least four
 // 128-wide macro steps per part. (One workgroup streams only a few tens of
-// GB/s, so long segments need the whole chip.)
+// GB/s, so long segments need the whole chip.) A shrink launch aims at two
+// workgroups per CU; the fused launch at fewer, which leaves slots to expand
+// workgroups, whose Y and B loads are then in flight while the shrink runs.
 constexpr int kShrinkTargetWorkgroups = 512;
-inline int shrink_ksplit64(int M, int d_in) {
+constexpr int kFusedShrinkTargetWorkgroups = 204;
+inline int shrink_ksplit64(int M, int d_in, int target = kShrinkTargetWorkgroups) {
     const int tiles = ceil_div(M, kTileRows64);
     const int nmacro = ceil_div(d_in, 128);
     if (tiles == 0) return 1;
-    int ks = (kShrinkTargetWorkgroups + tiles - 1) / tiles;
+    int ks = (target + tiles - 1) / tiles;
     ks = std::min(ks, 8);
     ks = std::min(ks, nmacro / 4);
     return std::max(ks, 1);
@@ -127,6 +130,15 @@ inline ShrinkPlan shrink_plan(int M, int d_in, int r, int dtype) {
     return P;
 }
 
+// The shrink work of a fused launch: as in a shrink launch, with the fused
+// launch's split of d_in for 64-row tiles (never more parts than a shrink
+// launch takes, so a shrink launch's item count bounds it).
+inline ShrinkPlan fused_shrink_plan(int M, int d_in, int r, int dtype) {
+    ShrinkPlan P = shrink_plan(M, d_in, r, dtype);
+    if (P.units && !P.small) P.ks = shrink_ksplit64(M, d_in, kFusedShrinkTargetWorkgroups);
+    return P;
+}
+
 // Shrink workspace (bf16 only, when the split is more than one part): the
 // header line, then one 128-byte counter line per shrink unit (its parts
 // arrived, then departed), then the units' partial results (unit x part).
@@ -167,7 +179,7 @@ struct FusedLayout {
 inline FusedLayout fused_layout(int M, int d_in, int d_out, int r, int dtype) {
     FusedLayout L;
     L.tiles = dtype == kBF16 ? ceil_div(M, kTileRows64) : 0;
-    L.plan = shrink_plan(M, d_in, r, dtype);
+    L.plan = fused_shrink_plan(M, d_in, r, dtype);
     L.copies = vector_col_tiles(d_out, dtype);
     L.tile_counters = kHeaderBytes;
     L.split_counters = align256(L.tile_counters + kCounterStride * sizeof(uint32_t) * (size_t)L.tiles);

@@ -302,7 +302,7 @@ static void size_cases() {
                             for (int q = 0; q <= SGMV_MAX_PROJECTIONS; ++q)
                                 p[q] = sgmv_projection{nullptr, nullptr, nullptr, nullptr, 4, di, dout};
                             const size_t l1 = sgmv_layer_workspace_bytes(p, 1, N, M, r, dt);
-                            CHECK(l1 == b, "one projection's layer workspace is its fused workspace");
+                            CHECK(l1 <= b, "one projection's layer workspace fits its single calls' workspace");
                             (void)sgmv_layer_workspace_bytes(p, SGMV_MAX_PROJECTIONS, N, M, r, dt);
                             CHECK(sgmv_layer_workspace_bytes(p, SGMV_MAX_PROJECTIONS + 1, N, M, r, dt) == 0,
                                   "too many projections");

@@ -467,6 +467,34 @@ def test_mid_length_segments(dev, oracle, dtype):
         assert int(torch.count_nonzero(WS)) == 0
 
 
+@pytest.mark.parametrize("r", [16, 64])
+def test_expand_tile_with_many_pieces(dev, oracle, r):
+    """A batch of short segments on average (so the MFMA expand tiles know
+    their pieces before they request anything) whose 64-row tiles meet up to
+    four long segments each, with distinct adapters: every piece after a
+    tile's first has its B tile requested while the previous piece is
+    worked on. Integer inputs, bitwise, split and fused, with the vector
+    segments in 8-row blocks around them."""
+    rng = np.random.Generator(np.random.PCG64(95))
+    WS = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    long_runs = [16, 16, 16, 16, 17, 23, 16, 20, 5, 9, 16, 16]
+    lengths = long_runs + [1] * 20 + [8, 3, 12, 1, 1]
+    ids = (np.arange(len(lengths)) % 7).astype(np.int32)
+    w = wl.Workload("pieces", int(sum(lengths)), 520, 1032, r, 2.0 * r, torch.bfloat16, 7,
+                    wl.segments_from_lengths(lengths), ids)
+    assert w.M < 16 * len(lengths)
+    wl.fill_tensors(w, rng)
+    wl.integer_case(rng, w)
+    c = to_device(w, dev)
+    V_ref, Y_ref = oracle_run(oracle, w)
+    V, Y = run_split(c, workspace=WS)
+    assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref)
+    want = oracle_bits(oracle, Y_ref, w.dtype)
+    assert np.array_equal(bits(Y), want)
+    assert np.array_equal(bits(run_fused(c, workspace=WS)), want)
+    assert int(torch.count_nonzero(WS)) == 0
+
+
 def test_graph_replays(dev, oracle):
     """The calls are stream-ordered and allocate nothing, so they can be
     captured in a HIP graph. Replays of a captured fused call and of a

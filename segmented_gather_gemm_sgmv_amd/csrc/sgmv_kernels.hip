@@ -1306,12 +1306,12 @@ static hipError_t launch_shrink_g(const ShrinkArgs &a, hipStream_t st) {
 }
 
 // Kernels are built per shrink tile kind (a bf16 batch of up to
-// kSmallBatchRows rows takes 16-row tiles, a larger one 64-row tiles);
+// small_batch_rows(r) rows takes 16-row tiles, a larger one 64-row tiles);
 // batches without the MFMA path take the 16-row build.
 template <typename T, int R>
 static hipError_t launch_shrink_t(const ShrinkArgs &a, hipStream_t st) {
     if constexpr (Elem<T>::kMfma) {
-        if (!small_tiles(a.M))
+        if (!small_tiles(a.M, R))
             return a.rows ? launch_shrink_g<T, R, true, false>(a, st) : launch_shrink_g<T, R, false, false>(a, st);
     }
     return a.rows ? launch_shrink_g<T, R, true, true>(a, st) : launch_shrink_g<T, R, false, true>(a, st);
@@ -1372,7 +1372,7 @@ static hipError_t launch_fused_g(const FusedArgs &a, hipStream_t st) {
 template <typename T, int R>
 static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     if constexpr (Elem<T>::kMfma) {
-        if (!small_tiles(a.M))
+        if (!small_tiles(a.M, R))
             return a.rows ? launch_fused_g<T, R, true, false>(a, st) : launch_fused_g<T, R, false, false>(a, st);
     }
     return a.rows ? launch_fused_g<T, R, true, true>(a, st) : launch_fused_g<T, R, false, true>(a, st);
@@ -1427,7 +1427,7 @@ static hipError_t launch_fused_layer_g(const LayerCall &a, hipStream_t st) {
 template <typename T, int R>
 static hipError_t launch_fused_layer_t(const LayerCall &a, hipStream_t st) {
     if constexpr (Elem<T>::kMfma) {
-        if (!small_tiles(a.M))
+        if (!small_tiles(a.M, R))
             return a.rows ? launch_fused_layer_g<T, R, true, false>(a, st)
                           : launch_fused_layer_g<T, R, false, false>(a, st);
     }

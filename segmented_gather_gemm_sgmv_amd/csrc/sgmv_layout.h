@@ -44,11 +44,14 @@ constexpr uint32_t kStatusBadOffsets = 2;   // seg_start decreases somewhere
 constexpr int kCounterStride = 32;  // uint32 words per counter line (128 bytes)
 
 // Which MFMA shrink tile a bf16 launch takes: 16-row tiles for batches of
-// up to kSmallBatchRows rows (few tiles: a handful of mid-length segments),
-// 64-row tiles above (many tiles: prefill batches), where sharing each A_k
-// chunk among 64 rows keeps the L1 traffic near the HBM bytes.
-constexpr int kSmallBatchRows = 2048;
-inline bool small_tiles(int M) { return M <= kSmallBatchRows; }
+// few tiles (a handful of mid-length segments), 64-row tiles for larger
+// ones (prefill batches), where sharing each A_k chunk among 64 rows keeps
+// the L1 traffic near the HBM bytes. The bound is where the two measured
+// even on MI355X (fused calls of 2 to 16 long segments): about 12 tiles of
+// 64 rows at r = 64, where a 16-row unit re-reads its 64 rank rows of A_k
+// for every 16 rows, and 16 tiles at smaller ranks.
+inline int small_batch_rows(int r) { return r >= 64 ? 768 : 1024; }
+inline bool small_tiles(int M, int r) { return M <= small_batch_rows(r); }
 
 // 16-row tiles: how many workgroups split d_in for each work item. Within a
 // workgroup the four waves already split d_in, so one workgroup per item is
@@ -117,7 +120,7 @@ struct ShrinkPlan {
 inline ShrinkPlan shrink_plan(int M, int d_in, int r, int dtype) {
     ShrinkPlan P{1, 0, 1, 0};
     if (dtype != kBF16) return P;
-    P.small = small_tiles(M) ? 1 : 0;
+    P.small = small_tiles(M, r) ? 1 : 0;
     if (P.small) {
         P.units = kShrinkPieces * shrink_groups(r) * ceil_div(M, kShrinkRows16);
         P.ks = shrink_ksplit16(M, d_in, r);

@@ -16,7 +16,7 @@
 //
 //  * shrink tile: D = X_rows . A_k^T (d_in x r), fp32 accumulation, in one
 //    of two tile kinds (see "Two shrink tiles" below): 16-row tiles whose
-//    four waves split d_in (batches of up to 2048 rows), or 64-row tiles with
+//    four waves split d_in (batches of up to 768 or 1024 rows), or 64-row tiles with
 //    one wave per 16 rows sharing A_k through LDS (larger batches). Both
 //    load X and A_k row-contiguously and reach the MFMA layout through LDS;
 //    d_in may be split over several workgroups whose partial tiles are

@@ -41,7 +41,7 @@ def _integer_workload(rng, lengths, ids, P, d_in, d_out, r):
 # Batches with a poisoned adapter (id 1) on a long segment that shares a
 # 16-row shrink tile and a 64-row expand tile with finite long segments, and
 # on a short (vector path) segment between finite short ones. The second
-# batch has more than 2048 rows, so its shrink runs on 64-row tiles.
+# batch has more than 2048 rows, so its shrink runs on 64-row tiles at every rank.
 POISON_CASES = {
     "small_batch": ([5, 20, 30, 3, 2, 40, 1, 16], [0, 1, 2, 1, 3, 4, 5, 2], 1024, 520),
     "large_batch": ([1000, 20, 30, 1100, 3, 2], [0, 1, 2, 3, 1, 4], 256, 264),

@@ -495,6 +495,32 @@ def test_expand_tile_with_many_pieces(dev, oracle, r):
     assert int(torch.count_nonzero(WS)) == 0
 
 
+@pytest.mark.parametrize("r,bound", [(64, 768), (16, 1024)])
+def test_tile_kind_bound(dev, oracle, r, bound):
+    """Batches just below and just above the row count where the MFMA shrink
+    changes from 16-row units to 64-row tiles (768 rows at r = 64, 1024
+    below): the same segments, extended by one row, give the oracle's
+    result bitwise on integer inputs through both kernels, split and
+    fused."""
+    rng = np.random.Generator(np.random.PCG64(96 + r))
+    WS = torch.zeros(1 << 23, dtype=torch.uint8, device=dev)
+    for M in (bound, bound + 1):
+        lengths = [M - 3 * 150 - 7, 150, 150, 150, 1, 2, 4]
+        ids = np.array([3, 0, 5, 1, 2, 4, 6], dtype=np.int32)
+        w = wl.Workload("bound", M, 264, 520, r, 2.0 * r, torch.bfloat16, 7, wl.segments_from_lengths(lengths), ids)
+        assert w.M == M
+        wl.fill_tensors(w, rng)
+        wl.integer_case(rng, w)
+        c = to_device(w, dev)
+        V_ref, Y_ref = oracle_run(oracle, w)
+        V, Y = run_split(c, workspace=WS)
+        assert np.array_equal(V.cpu().numpy().astype(np.float64), V_ref), M
+        want = oracle_bits(oracle, Y_ref, w.dtype)
+        assert np.array_equal(bits(Y), want), M
+        assert np.array_equal(bits(run_fused(c, workspace=WS)), want), M
+        assert int(torch.count_nonzero(WS)) == 0
+
+
 def test_graph_replays(dev, oracle):
     """The calls are stream-ordered and allocate nothing, so they can be
     captured in a HIP graph. Replays of a captured fused call and of a
